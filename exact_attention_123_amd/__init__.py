@@ -1,0 +1,138 @@
+"""Python binding of the fused exact-attention forward for MI355X (gfx950).
+
+The computation runs entirely in the HIP library ``libattn.so`` (C ABI in
+``include/attn.h``); this module only marshals arguments.  PyTorch provides
+device memory and the current stream.
+
+    from exact_attention_123_amd import forward
+    o, lse = forward(q, k, v, causal=True)        # q, k, v: [B, H, T, d] on cuda
+
+The raw entry points ``attn_fwd`` / ``attn_fwd_f32`` take integer device
+addresses and sizes exactly as the C functions do.  If the library has not
+been built, importing works but every call raises ``LibraryNotBuilt``: there
+is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "forward", "attn_fwd", "attn_fwd_f32", "kernel_name", "status_string",
+    "AttnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "STATUS",
+    "flops",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_ARG", 7: "ATTN_ERR_DEVICE",
+    8: "ATTN_ERR_LAUNCH",
+}
+
+# The C prototypes from include/attn.h.
+EXPORTS = {
+    "attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4
+                 + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_fwd_f32": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4
+                     + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_kernel_name": (ctypes.c_char_p, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
+}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libattn.so once and attach the prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise LibraryNotBuilt(
+            f"{path} is missing; build it with `python -m exact_attention_123_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().attn_status_string(code).decode()
+
+
+def kernel_name(is_f32: bool, d: int, causal: bool):
+    n = load_library().attn_kernel_name(int(bool(is_f32)), int(d), int(bool(causal)))
+    return None if n is None else n.decode()
+
+
+def attn_fwd(q, k, v, o, lse, B, H, T, d, causal, scale, stream=0) -> int:
+    """Raw bf16 entry point: integer device addresses, returns the status."""
+    return load_library().attn_fwd(q, k, v, o, lse, B, H, T, d, int(causal), float(scale),
+                                   stream or None)
+
+
+def attn_fwd_f32(q, k, v, o, lse, B, H, T, d, causal, scale, stream=0) -> int:
+    """Raw fp32 entry point: integer device addresses, returns the status."""
+    return load_library().attn_fwd_f32(q, k, v, o, lse, B, H, T, d, int(causal),
+                                       float(scale), stream or None)
+
+
+def flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
+    """Counted FLOPs of one forward: the two T x T x d contractions,
+    4*T*T*d per head, halved under a causal mask."""
+    f = 4.0 * B * H * T * T * d
+    return f / 2 if causal else f
+
+
+def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
+            stream=None):
+    """Fused attention forward on torch tensors [B, H, T, d] (bf16 or fp32).
+
+    Returns (o, lse): o has q's dtype and shape; lse is float32 [B, H, T].
+    Runs on ``stream`` (a torch.cuda.Stream) or the current stream.
+    """
+    import torch
+
+    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
+        raise ValueError("q, k, v must all have shape [B, H, T, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous CUDA tensors")
+    B, H, T, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    fn = attn_fwd_f32 if q.dtype == torch.float32 else attn_fwd
+    with torch.cuda.device(q.device):
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                B, H, T, d, causal, scale, s)
+    if st != 0:
+        raise AttnError(st, status_string(st))
+    return out, lse

@@ -1,0 +1,109 @@
+/*
+ * attn.h -- C ABI of the fused, I/O-aware forward pass of exact scaled
+ * dot-product attention on AMD Instinct MI355X (gfx950).
+ *
+ * For every (batch b, head h) the library computes, for queries Q, keys K
+ * and values V of shape T x d,
+ *
+ *   S   = scale * Q K^T                 scores, rows = queries, cols = keys
+ *   S_ij = -inf for j > i               only when causal = 1
+ *   P   = row softmax of S              exp(S_ij) / sum_j exp(S_ij)
+ *   O   = P V                           T x d output
+ *   LSE_i = ln sum_j exp(S_ij)          natural-log "exponential sum"
+ *
+ * as defined on "Attention Mechanism: Computation & Memory Patterns"
+ * (section 1, the attention equation and its three steps) and "Why Attention
+ * Is Difficult to Optimize" ("The Attention Computation Flow", Figure 1:
+ * scale, then causal mask, then softmax, then PV).  The T x T matrices S and
+ * P never reach device memory: the kernel walks key/value tiles with an
+ * online softmax (running max, running normaliser, rescaled fp32 output
+ * accumulator), as described on "Attention Mechanism: Computation & Memory
+ * Patterns" (section 3, tiling and online softmax) and "FlashAttention --
+ * avoid writing the giant intermediate" ("Tiling and an incremental
+ * normalization").  LSE is an extra per-row output the pages do not define;
+ * it is the natural log of the row's exponential sum of scaled, masked
+ * scores.
+ *
+ * Layout.  q, k, v, o are contiguous [B][H][T][d] arrays (d innermost,
+ * element (b,h,t,c) at ((b*H + h)*T + t)*d + c); lse is a contiguous
+ * [B][H][T] float array.  All pointers are device pointers.
+ *
+ * Ownership.  The caller owns every buffer.  The library allocates, frees
+ * and keeps no device memory and uses no workspace.  It holds no mutable
+ * state other than a per-device cache of the architecture check, and may be
+ * called from several host threads.
+ *
+ * Asynchrony.  Calls enqueue one kernel on `stream` (NULL = the null
+ * stream) and return; they never synchronise.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; on a
+ * validation error nothing is launched and the outputs are untouched.  An
+ * unsupported head dimension or device is an error, never a fallback.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a pointer is NULL for a non-empty problem      */
+  ATTN_ERR_SHAPE = 2,       /* B, H or T negative, or sizes overflow limits   */
+  ATTN_ERR_UNSUPPORTED = 3, /* head dimension d is not 64 or 128              */
+  ATTN_ERR_SCALE = 4,       /* scale is NaN or infinite                       */
+  ATTN_ERR_ALIGN = 5,       /* q/k/v/o not 16-byte or lse not 4-byte aligned  */
+  ATTN_ERR_ARG = 6,         /* causal not 0/1, or an output overlaps a buffer */
+  ATTN_ERR_DEVICE = 7,      /* the current device is not gfx950               */
+  ATTN_ERR_LAUNCH = 8       /* the HIP runtime reported an error at launch    */
+} attn_status;
+
+/*
+ * bfloat16 forward.  q, k, v: const __hip_bfloat16 [B][H][T][d]; o:
+ * __hip_bfloat16 [B][H][T][d], written with round-to-nearest-even; lse:
+ * float [B][H][T].  Scores and all softmax state are fp32; both
+ * contractions run on bf16 MFMA with fp32 accumulation, and P is rounded to
+ * bf16 (nearest-even) before the PV contraction.
+ *   B, H, T >= 0 (B*H*T == 0: nothing to do, ATTN_OK, pointers unchecked);
+ *          (T + 256) * d * sizeof(element) < 2^31 (one head under 2 GiB) and
+ *          B*H*ceil(T/128) < 2^31;
+ *   d in {64, 128};
+ *   causal: 0 = full attention, 1 = key j visible to query i iff j <= i;
+ *   scale: any finite multiplier of Q K^T (usually 1/sqrt(d)); it is applied
+ *          to the fp32 scores, never folded into bf16 inputs.
+ * Outputs must not overlap each other or any input.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int64_t B, int64_t H, int64_t T, int64_t d,
+                     int causal, float scale, hipStream_t stream);
+
+/*
+ * float32 forward: the same contract with float elements in q, k, v, o.
+ * Both contractions use fp32 MFMA (no reduced-precision inputs); P stays
+ * fp32.
+ */
+attn_status attn_fwd_f32(const float* q, const float* k, const float* v,
+                         float* o, float* lse, int64_t B, int64_t H,
+                         int64_t T, int64_t d, int causal, float scale,
+                         hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* attn_status_string(attn_status s);
+
+/*
+ * Name of the kernel instance attn_fwd (is_f32 = 0) or attn_fwd_f32
+ * (is_f32 = 1) launches for head dimension d and the causal flag, e.g.
+ * "attn_fwd_bf16_d128_causal_br128_bc64_w4", so that a caller can log which
+ * kernel ran.  NULL if the combination is unsupported.
+ */
+const char* attn_kernel_name(int is_f32, int64_t d, int causal);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,117 @@
+"""The C-ABI library on the host (CPU only): it loads, exports every function
+include/attn.h declares, and rejects bad arguments before any HIP call.
+
+No call here reaches a kernel launch: every argument set is invalid (or
+empty), and validation returns before the library touches the HIP runtime.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_attention_123_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ea.LIB_PATH),
+                                reason="libattn.so not built")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+# The argument sets below use fake device addresses and are all invalid, so
+# validation rejects them before any launch.  They are still kept off
+# machines with a GPU: a validation bug there would launch a kernel on fake
+# addresses.
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer checks run GPU-less")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_exports():
+    assert declared_functions() == sorted(ea.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ea.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings_and_kernel_names():
+    for code in range(9):
+        assert ea.status_string(code)
+    assert ea.status_string(99) == "unknown status"
+    assert ea.kernel_name(False, 128, True).startswith("attn_fwd_bf16_d128_causal")
+    assert ea.kernel_name(False, 64, False).startswith("attn_fwd_bf16_d64_full")
+    assert ea.kernel_name(True, 64, True).startswith("attn_fwd_f32_d64_causal")
+    assert ea.kernel_name(False, 96, True) is None
+
+
+A = 0x10000  # 16-byte aligned fake addresses, never dereferenced
+
+
+def call(fn, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, T=8, d=64, causal=1,
+         scale=0.125):
+    return fn(q, k, v, o, lse, B, H, T, d, causal, scale)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("fn", [ea.attn_fwd, ea.attn_fwd_f32], ids=["bf16", "f32"])
+def test_validation_errors(fn):
+    assert call(fn, q=0) == 1
+    assert call(fn, lse=0) == 1
+    assert call(fn, B=-1) == 2
+    assert call(fn, T=-5) == 2
+    assert call(fn, T=(1 << 30) + 1) == 2
+    assert call(fn, B=1 << 20, H=1 << 20) == 2
+    # one head of q (or k, v, o) must stay under 2 GiB
+    assert call(fn, T=(1 << 31) // 256, d=128) == 2
+    for d in (0, 32, 96, 127, 256):
+        assert call(fn, d=d) == 3
+    for s in (math.nan, math.inf, -math.inf):
+        assert call(fn, scale=s) == 4
+    assert call(fn, q=A + 2) == 5
+    assert call(fn, o=4 * A + 8) == 5
+    assert call(fn, lse=5 * A + 2) == 5
+    assert call(fn, causal=2) == 6
+    assert call(fn, causal=-1) == 6
+    assert call(fn, o=A) == 6          # output aliases q
+    assert call(fn, lse=4 * A) == 6    # lse overlaps o
+
+
+@pytest.mark.parametrize("fn", [ea.attn_fwd, ea.attn_fwd_f32], ids=["bf16", "f32"])
+def test_empty_problem_is_a_no_op(fn):
+    for kw in (dict(B=0), dict(H=0), dict(T=0)):
+        assert call(fn, q=0, k=0, v=0, o=0, lse=0, **kw) == 0
+
+
+@no_gpu_only
+def test_error_precedence_shape_before_pointers():
+    # a negative size is reported even when pointers are also bad
+    assert call(ea.attn_fwd, q=0, B=-1) == 2
+
+
+def test_flops_convention():
+    # 4*T^2*d per head, halved under a causal mask
+    assert ea.flops(1, 32, 8192, 128, True) == pytest.approx(549.755813888e9)
+    assert ea.flops(4, 16, 4096, 128, False) == pytest.approx(549.755813888e9)
+    assert ea.flops(1, 1, 256, 64, True) == 2 * 256 * 256 * 64
