@@ -49,6 +49,7 @@
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -101,41 +102,62 @@ __device__ __forceinline__ void block_coords(int BH, int nqb, int& bh, int& qb) 
   bh = id % BH;
 }
 
-// Online-softmax update for one wave's tile of scores.
-//   x   : NKT accumulator tiles of scaled scores (log2 units), masked = -inf
-//   m   : running max (log2 units, same in both lane halves)
-//   l   : lane-partial running normaliser
-//   o   : NDT output accumulator tiles
-// On return x holds p = exp2(x - m_new).
+// Max of x over the lane pair (l, l ^ 32) that holds one query's scores.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Rescaling threshold of the running max, in log2 units.  The running max m
+// is only raised when a tile's max exceeds it by more than this, so p =
+// exp2(c*s - m) stays below 2^kLazyRescale and the output accumulator and
+// normaliser are rescaled only on those (rare, wave-uniform) occasions.  The
+// result is the same softmax: the common factor cancels in acc / l.
+constexpr float kLazyRescale = 8.0f;
+
+// Online-softmax update for one wave's tile of scores ("FlashAttention --
+// avoid writing the giant intermediate", "Tiling and an incremental
+// normalization"; "Attention Mechanism", section 3, online softmax).
+//   s   : NKT accumulator tiles of scores, masked entries = -inf; the score
+//         in log2 units is cm * s
+//   m   : running max in log2 units (same value in both lane halves)
+//   l, w: lane-partial running normalisers, relative to m
+//   o   : NDT output accumulator tiles, relative to m
+// On return s holds p = exp2(cm * s - m); l, w and o are rescaled when m
+// rises, and the caller adds the tile's p to l and w.
 template <int NKT, int NDT>
-__device__ __forceinline__ void online_softmax_update(f32x16_t (&x)[NKT], float& m, float& l,
-                                                      f32x16_t (&o)[NDT]) {
-  float mx = x[0][0];
+__device__ __forceinline__ void online_softmax_update(f32x16_t (&s)[NKT], float cm, float& m,
+                                                      float& l, float& w, f32x16_t (&o)[NDT]) {
+  float mx = s[0][0];
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kt][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m, mx);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+  const float mt = pair_max(mx) * cm;
+  // Raise a row's running max only when the tile's max outgrows it by more
+  // than the threshold (m = -inf on the first tile always does).  The
+  // decision is per row, so a row's result never depends on other rows; the
+  // wave only skips the rescaling loop when no row needs it (alpha = 1 is
+  // exact for the rows that do not).
+  const bool grow = mt > m + kLazyRescale;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float alpha = !grow ? 1.0f : (m == -INFINITY) ? 0.0f : exp2_hw(m - mt);
+    l *= alpha;
+    w *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    m = grow ? mt : m;
+  }
   // A row with no visible key so far keeps m = -inf; subtract 0 instead so
   // that its terms are exp2(-inf) = 0 rather than NaN.
-  const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-  const float alpha = exp2_hw(m - base);
-  float psum = 0.0f;
+  const float base = (m == -INFINITY) ? 0.0f : m;
 #pragma unroll
   for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2_hw(x[kt][r] - base);
-      x[kt][r] = p;
-      psum += p;
-    }
-  l = l * alpha + psum;
-  m = m_new;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    for (int r = 0; r < 16; ++r) s[kt][r] = exp2_hw(fmaf(s[kt][r], cm, -base));
 }
 
 // ---------------------------------------------------------------------------
@@ -151,19 +173,24 @@ struct Bf16Tile {
   static constexpr int VS = BC + 8;          // V^T row stride in LDS (elements)
   static constexpr int KCH = BC * D / 8 / kThreads;  // 16-byte K chunks per thread
   static constexpr int KPT = BC * D / 8 / kThreads;  // keys per thread (V transpose)
+  static constexpr int NKB = BC / KPT;       // key blocks per tile (V transpose)
   static constexpr int DCH = D / 8;          // 16-byte chunks per row
 };
 
-template <int D, bool CAUSAL>
+// PRESCALE: multiply the scores by c before the softmax (any sign of c);
+// otherwise (c > 0) the multiply is folded into the exponent's fma and the
+// max is taken over the raw scores.
+template <int D, bool CAUSAL, bool PRESCALE>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, float c) {
   using C = Bf16Tile<D>;
   constexpr int BC = C::BC, NKT = C::NKT, NDS = C::NDS, NDT = C::NDT;
   constexpr int KS = C::KS, VS = C::VS, KCH = C::KCH, KPT = C::KPT, DCH = C::DCH;
+  constexpr int NKB = C::NKB;
   constexpr int ROWB = D * 2;  // bytes per row of Q, K, V, O
   static_assert(KCH * kThreads * 8 == BC * D, "K tile split");
-  static_assert(KPT * (kThreads / DCH) == BC, "V tile split");
+  static_assert(NKB * (D / 8) == kThreads, "V tile split");
 
   __shared__ __attribute__((aligned(16))) __bf16 sK[2][BC * KS];
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][D * VS];
@@ -197,7 +224,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
   // Staging registers for the next tile's global loads.
   u32x4_t kreg[KCH], vreg[KPT];
-  const int vdb = tid % DCH, vkb = tid / DCH;  // V transpose: 8 d x KPT keys
+  // V transpose: each thread owns 8 d x KPT keys; the 16 (or 32) lanes of a
+  // group take consecutive key blocks of one d block, so that each V^T row
+  // they store is one contiguous, bank-conflict-free run.
+  const int vkb = tid % NKB, vdb = tid / NKB;
   auto gload = [&](int t) {
     const int kv0 = t * BC;
 #pragma unroll
@@ -237,7 +267,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   f32x16_t oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f, w_run = 0.0f;
   const int krow = key_row_perm(j);
 
   // One tile: S^T = K Q^T, scale and mask, online softmax, O^T += V^T P^T.
@@ -255,10 +285,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
             *reinterpret_cast<const bf16x8_t*>(kb + (kt * 32 + krow) * KS + 16 * s + 8 * h);
         x[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], x[kt], 0, 0, 0);
       }
+    if constexpr (PRESCALE) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[kt][r] *= c;
+        for (int r = 0; r < 16; ++r) x[kt][r] *= c;
+    }
     if constexpr (MASK) {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
@@ -268,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
           if (key >= T || (CAUSAL && key > qg)) x[kt][r] = -INFINITY;
         }
     }
-    online_softmax_update<NKT, NDT>(x, m_run, l_run, oacc);
+    online_softmax_update<NKT, NDT>(x, PRESCALE ? 1.0f : c, m_run, l_run, w_run, oacc);
     const __bf16* vb = sV[buf];
 #pragma unroll
     for (int kt = 0; kt < NKT; ++kt)
@@ -277,6 +309,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         bf16x8_t pb;
 #pragma unroll
         for (int u = 0; u < 8; ++u) pb[u] = (__bf16)x[kt][8 * a + u];
+        // Two normalisers: l_run sums the fp32 weights (it gives LSE), and
+        // w_run sums exactly the bf16 weights the PV MFMA uses, so that O =
+        // sum p'v / sum p' is a convex combination of V rows (bf16 rounding
+        // of a dominant weight then cancels instead of scaling O).
+        const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u) l_run += x[kt][8 * a + u];
+        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one2, w_run, false);
+        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, w_run, false);
+        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, w_run, false);
+        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, w_run, false);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const bf16x8_t vv = *reinterpret_cast<const bf16x8_t*>(
@@ -307,8 +350,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
   // Epilogue: combine the two lane halves' partial normalisers.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float w_tot = w_run + __shfl_xor(w_run, 32);
   if (qg < T) {
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / w_tot;
     __bf16* orow = O + head + (size_t)qg * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -429,7 +473,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
           if (key >= T || (CAUSAL && key > qg)) x[0][r] = -INFINITY;
         }
       }
-      online_softmax_update<1, NDT>(x, m_run, l_run, oacc);
+      float unused = 0.0f;  // fp32 P is not rounded: one normaliser serves O and LSE
+      online_softmax_update<1, NDT>(x, 1.0f, m_run, l_run, unused, oacc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) l_run += x[0][r];
       const float* vb = sV[buf];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -534,11 +581,16 @@ attn_status launch(const void* kernel, const Elem* q, const Elem* k, const Elem*
   return ATTN_OK;
 }
 
-const void* bf16_kernel(int64_t d, int causal) {
-  if (d == 64) return causal ? (const void*)attn_fwd_bf16_kernel<64, true>
-                             : (const void*)attn_fwd_bf16_kernel<64, false>;
-  return causal ? (const void*)attn_fwd_bf16_kernel<128, true>
-                : (const void*)attn_fwd_bf16_kernel<128, false>;
+template <bool PRESCALE>
+const void* bf16_kernel_p(int64_t d, int causal) {
+  if (d == 64) return causal ? (const void*)attn_fwd_bf16_kernel<64, true, PRESCALE>
+                             : (const void*)attn_fwd_bf16_kernel<64, false, PRESCALE>;
+  return causal ? (const void*)attn_fwd_bf16_kernel<128, true, PRESCALE>
+                : (const void*)attn_fwd_bf16_kernel<128, false, PRESCALE>;
+}
+
+const void* bf16_kernel(int64_t d, int causal, float scale) {
+  return scale > 0.0f ? bf16_kernel_p<false>(d, causal) : bf16_kernel_p<true>(d, causal);
 }
 
 const void* f32_kernel(int64_t d, int causal) {
@@ -559,7 +611,7 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   attn_status st = validate(q, k, v, o, lse, B, H, T, d, causal, scale, 2, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  return launch<__bf16>(bf16_kernel(d, causal), (const __bf16*)q, (const __bf16*)k,
+  return launch<__bf16>(bf16_kernel(d, causal, scale), (const __bf16*)q, (const __bf16*)k,
                         (const __bf16*)v, (__bf16*)o, lse, B, H, T, scale, stream);
 }
 
