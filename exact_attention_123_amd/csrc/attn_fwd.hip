@@ -163,20 +163,74 @@ __device__ __forceinline__ void online_softmax_update(f32x16_t (&s)[NKT], float 
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
 template <int D>
 struct Bf16Tile {
-  static constexpr int BC = 64;              // keys per tile
-  static constexpr int NKT = BC / 32;        // 32-key accumulator tiles
-  static constexpr int NDS = D / 16;         // k-steps of the QK^T MFMA
-  static constexpr int NDT = D / 32;         // 32-row d tiles of O^T
-  static constexpr int KS = D + 8;           // K row stride in LDS (elements)
-  static constexpr int VS = BC + 8;          // V^T row stride in LDS (elements)
-  static constexpr int KCH = BC * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int KPT = BC * D / 8 / kThreads;  // keys per thread (V transpose)
-  static constexpr int NKB = BC / KPT;       // key blocks per tile (V transpose)
-  static constexpr int DCH = D / 8;          // 16-byte chunks per row
+  static constexpr int BC = 64;             // keys per tile
+  static constexpr int NKT = BC / 32;       // 32-key score tiles
+  static constexpr int NKC = BC / 16;       // 16-key steps of the PV MFMA
+  static constexpr int NDS = D / 16;        // 16-wide d steps of the QK MFMA
+  static constexpr int NDT = D / 32;        // 32-row d tiles of O^T
+  static constexpr int RB = D * 2;          // bytes per row of Q, K, V, O
+  static constexpr int NCH = D / 8;         // 16-byte chunks per row
+  // K tile in LDS: each row is followed by one unused 16-byte slot, so rows
+  // sit NCH + 1 (an odd number of) slots apart and the 16 rows that one
+  // 16-lane phase of a 128-bit LDS read touches fall in 16 different banks.
+  static constexpr int KSLOT = NCH + 1;
+  static constexpr int KROWB = KSLOT * 16;
+  static constexpr int KBYTES = BC * KROWB;
+  static constexpr int KDMA = KBYTES / 1024;      // 1 KiB direct-to-LDS blocks
+  static constexpr int KPER = (KDMA + 3) / 4;     // blocks per wave (at most)
+  // V tile in LDS: unpadded rows with an XOR swizzle of the 16-byte chunks
+  // (see v_chunk_swizzle), 1 KiB blocks of RPK rows.
+  static constexpr int VBYTES = BC * RB;
+  static constexpr int VDMA = VBYTES / 1024;
+  static constexpr int VPER = VDMA / 4;
+  static constexpr int RPK = 1024 / RB;
+  static constexpr int RPB = 256 / RB;      // rows per 256-byte bank cycle
+  static_assert(KBYTES % 1024 == 0 && VBYTES % 4096 == 0, "tile split");
 };
 
+// XOR applied to the 16-byte chunk index of V row r.  The transposing LDS
+// read of the PV operand makes each half-wave read 4 consecutive rows x 4
+// consecutive chunks; flipping chunk bits 2-3 by the row's position within
+// 4 rows (counted in 256-byte bank cycles) puts those 16 chunks in 16
+// different bank groups.
+template <int D>
+__host__ __device__ constexpr int v_chunk_swizzle(int r) {
+  using C = Bf16Tile<D>;
+  return 4 * ((r / C::RPB) % (C::NCH / 4));
+}
+
+// Exact sum of the lane's fp32 values in four independent chains.
+template <int N>
+__device__ __forceinline__ float sum_tree(const float* x) {
+  float a = x[0], b = x[1], c = x[2], d = x[3];
+#pragma unroll
+  for (int i = 4; i < N; i += 4) {
+    a += x[i];
+    b += x[i + 1];
+    c += x[i + 2];
+    d += x[i + 3];
+  }
+  return (a + b) + (c + d);
+}
+
+// One wave owns 32 query rows; the workgroup (4 waves) 128 rows of one head.
+// Key/value tiles of 64 keys stream through LDS, written by direct-to-LDS
+// buffer loads (no staging registers) two tiles (K) and one tile (V) ahead
+// of their use.
+//
+// The online softmax runs on score sub-tiles of 32 keys, software-pipelined
+// per wave: while the VALU computes the softmax of sub-tile k, the matrix
+// cores compute S_{k+1} = K_{k+1} Q^T and O^T += V_{k-1}^T P_{k-1}^T, all
+// in one straight-line block.  The running max is raised lazily (see
+// kLazyRescale), so the accumulator rescale is a rare, wave-uniform branch
+// between blocks (after P_{k-1} V_{k-1} is in, before P_k V_k).
+//
 // PRESCALE: multiply the scores by c before the softmax (any sign of c);
 // otherwise (c > 0) the multiply is folded into the exponent's fma and the
 // max is taken over the raw scores.
@@ -185,167 +239,297 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, float c) {
   using C = Bf16Tile<D>;
-  constexpr int BC = C::BC, NKT = C::NKT, NDS = C::NDS, NDT = C::NDT;
-  constexpr int KS = C::KS, VS = C::VS, KCH = C::KCH, KPT = C::KPT, DCH = C::DCH;
-  constexpr int NKB = C::NKB;
-  constexpr int ROWB = D * 2;  // bytes per row of Q, K, V, O
-  static_assert(KCH * kThreads * 8 == BC * D, "K tile split");
-  static_assert(NKB * (D / 8) == kThreads, "V tile split");
+  constexpr int BC = C::BC, NDS = C::NDS, NDT = C::NDT;
+  constexpr int RB = C::RB, NCH = C::NCH, KSLOT = C::KSLOT, KROWB = C::KROWB;
+  constexpr int KDMA = C::KDMA, KPER = C::KPER, VPER = C::VPER, RPK = C::RPK;
+  static_assert(BC == 64, "two 32-key score sub-tiles per LDS tile");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][BC * KS];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][D * VS];
+  // LDS: two K and two V buffers, separate objects so that the compiler can
+  // tell the direct-to-LDS writes into one buffer from reads of another.
+  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, h = lane >> 5;
   int bh, qb;
   block_coords(BH, nqb, bh, qb);
   const size_t head = (size_t)bh * (size_t)T * D;
-  const int head_bytes = T * ROWB;
-  const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + head, head_bytes);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + head, head_bytes);
+  const int head_bytes = T * RB;
+  const __bf16* Kh = K + head;
+  const __bf16* Vh = V + head;
   const int q0 = qb * kBR;
-  const int q0w = q0 + wave * 32;
-  const int qg = q0w + j;
+  const int qg = q0 + wave * 32 + j;
 
   // Q fragment: B operand of S^T = K Q^T; lane (j, h) holds
   // Q[qg][16 s + 8 h .. +8] for every k-step s.  Rows >= T read as zero.
   bf16x8_t qf[NDS];
+  {
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + head, head_bytes);
 #pragma unroll
-  for (int s = 0; s < NDS; ++s)
-    qf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rQ, qg * ROWB + (16 * s + 8 * h) * 2));
+    for (int s = 0; s < NDS; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rQ, qg * RB + (16 * s + 8 * h) * 2));
+  }
 
   const int kv_end = CAUSAL ? min(T, q0 + kBR) : T;
   const int ntiles = (kv_end + BC - 1) / BC;
-  // Tiles below n_full need no mask: every key is < T and, when causal, no
-  // later than the workgroup's first query.
-  const int n_full = (CAUSAL ? min(q0 + 1, T) : T) / BC;
+  // Score sub-tiles (32 keys) below nfs need no mask: every key is < T and,
+  // when causal, no later than the workgroup's first query.
+  const int nfs = (CAUSAL ? min(q0 + 1, T) : T) / 32;
 
-  // Staging registers for the next tile's global loads.
-  u32x4_t kreg[KCH], vreg[KPT];
-  // V transpose: each thread owns 8 d x KPT keys; the 16 (or 32) lanes of a
-  // group take consecutive key blocks of one d block, so that each V^T row
-  // they store is one contiguous, bank-conflict-free run.
-  const int vkb = tid % NKB, vdb = tid / NKB;
-  auto gload = [&](int t) {
+  // Direct-to-LDS loads.  A 1 KiB block is written by one wave instruction,
+  // lane L's 16 bytes landing at block offset 16 L; each lane picks the
+  // global chunk that belongs there.  K: block b holds padded slots
+  // 64 b .. 64 b + 63 (slot u = row u / KSLOT, chunk u % KSLOT; the pad slot
+  // re-reads the row's last chunk).  Wave w writes blocks w, w + 4, ...
+  int koff[KPER];
+#pragma unroll
+  for (int n = 0; n < KPER; ++n) {
+    const int u = 64 * (wave + 4 * n) + lane;
+    const int r = u / KSLOT, ch = u % KSLOT;
+    koff[n] = r * RB + 16 * min(ch, NCH - 1);
+  }
+  // V: wave w writes blocks VPER w .. VPER w + VPER - 1 (block b holds rows
+  // RPK b .. RPK b + RPK - 1).
+  int voff;
+  {
+    const int r = RPK * VPER * wave + lane / NCH;
+    const int pc = lane % NCH;
+    voff = r * RB + 16 * (pc ^ v_chunk_swizzle<D>(r));
+  }
+  auto dma_k = [&](char* buf, int t) __attribute__((always_inline)) {
     const int kv0 = t * BC;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(Kh + (size_t)kv0 * D, max(head_bytes - kv0 * RB, 0));
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = i * kThreads + tid;
-      kreg[i] = buf_load16(rK, (kv0 + ch / DCH) * ROWB + (ch % DCH) * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) vreg[i] = buf_load16(rV, (kv0 + vkb * KPT + i) * ROWB + vdb * 16);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ch = i * kThreads + tid;
-      *reinterpret_cast<u32x4_t*>(&sK[buf][(ch / DCH) * KS + (ch % DCH) * 8]) = kreg[i];
-    }
-    // Transpose 8 d x KPT keys in registers and store rows d of V^T.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      unsigned int packed[KPT / 2];
-#pragma unroll
-      for (int i = 0; i < KPT / 2; ++i) {
-        const unsigned int lo = (vreg[2 * i][w] >> sh) & 0xffffu;
-        const unsigned int hi = (vreg[2 * i + 1][w] >> sh) & 0xffffu;
-        packed[i] = lo | (hi << 16);
-      }
-      __bf16* dst = &sV[buf][(vdb * 8 + e) * VS + vkb * KPT];
-      if constexpr (KPT == 4) {
-        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{packed[0], packed[1]};
-      } else {
-        *reinterpret_cast<unsigned int*>(dst) = packed[0];
-      }
+    for (int n = 0; n < KPER; ++n) {
+      // (a plain local: host-side template instantiation drops the kernel
+      // when an array element is passed to this builtin directly)
+      const int off = koff[n];
+      if (wave + 4 * n < KDMA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + 1024 * (wave + 4 * n)), 16,
+                                                 off, 0, 0, 0);
     }
   };
+  auto dma_v = [&](char* buf, int t) __attribute__((always_inline)) {
+    const int kv0 = t * BC;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(Vh + (size_t)kv0 * D, max(head_bytes - kv0 * RB, 0));
+    // The instruction offset (1024 n) advances both the global and the LDS
+    // address; voffset only moves the global one.
+    lds_void_t* dst = (lds_void_t*)(buf + 1024 * VPER * wave);
+    auto block = [&](auto n) __attribute__((always_inline)) {
+      constexpr int N = decltype(n)::value;
+      if constexpr (N < VPER) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 1024 * N, 0);
+    };
+    static_assert(VPER <= 4, "V blocks per wave");
+    block(std::integral_constant<int, 0>{});
+    block(std::integral_constant<int, 1>{});
+    block(std::integral_constant<int, 2>{});
+    block(std::integral_constant<int, 3>{});
+  };
+
+  // LDS read addresses.  K (A operand of the QK MFMA): lane (j, h) reads row
+  // 32 half + perm(j), chunk 2 s + h.
+  const int kaddr = key_row_perm(j) * KROWB + 16 * h;
+  // V (A operand of the PV MFMA, V^T): ds_read_b64_tr_b16 gives lane i of a
+  // 16-lane group element (i % 4) of the 8 bytes read by lane 4 e + i / 4 of
+  // the group, in slot e.  Lane l of group g reads V[row][d .. d + 3] with
+  // row = 8 (g / 2) + l / 4 (+ 16 kc + 4 half) and d = 32 dt + 16 (g % 2) +
+  // 4 (l % 4), so lane i of the group receives V[row0 + e][32 dt + 16 (g % 2)
+  // + i] for e = 0..3: four consecutive keys of one d, i.e. V^T.  The
+  // swizzle only flips chunk bits 2-3, i.e. the dt field, so the address of
+  // tile dt is vaddr0 ^ (64 dt).
+  int vaddr0;
+  {
+    const int g = lane >> 4, l = lane & 15;
+    const int r = 8 * (g >> 1) + (l >> 2);
+    const int ch = 2 * (g & 1) + ((l >> 1) & 1);
+    vaddr0 = r * RB + 16 * (ch ^ v_chunk_swizzle<D>(r)) + 8 * (l & 1);
+  }
 
   f32x16_t oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.0f, w_run = 0.0f;
-  const int krow = key_row_perm(j);
+  const float cm = PRESCALE ? 1.0f : c;
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // One tile: S^T = K Q^T, scale and mask, online softmax, O^T += V^T P^T.
-  auto compute = [&](int buf, int kv0, auto masked) {
-    constexpr bool MASK = decltype(masked)::value;
-    f32x16_t x[NKT];
+  // S^T of the 32-key half `half` of the K tile in `kb`.
+  auto qk = [&](const char* kb, int half, f32x16_t& sn) __attribute__((always_inline)) {
+    sn = f32x16_t{};
+    const char* base = kb + kaddr;
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) x[kt] = f32x16_t{};
-    const __bf16* kb = sK[buf];
-#pragma unroll
-    for (int s = 0; s < NDS; ++s)
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(kb + (kt * 32 + krow) * KS + 16 * s + 8 * h);
-        x[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], x[kt], 0, 0, 0);
-      }
-    if constexpr (PRESCALE) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[kt][r] *= c;
+    for (int s = 0; s < NDS; ++s) {
+      const bf16x8_t a =
+          *reinterpret_cast<const bf16x8_t*>(base + half * 32 * KROWB + 32 * s);
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sn, 0, 0, 0);
     }
-    if constexpr (MASK) {
+  };
+
+  // O^T += V^T P^T for the 32-key half `half` of the V tile in `vb`.
+  auto pv = [&](const char* vb, int half, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kt = 0; kt < NKT; ++kt)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + acc_key_perm(r, h);
-          if (key >= T || (CAUSAL && key > qg)) x[kt][r] = -INFINITY;
-        }
-    }
-    online_softmax_update<NKT, NDT>(x, PRESCALE ? 1.0f : c, m_run, l_run, w_run, oacc);
-    const __bf16* vb = sV[buf];
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pb[u] = (__bf16)x[kt][8 * a + u];
-        // Two normalisers: l_run sums the fp32 weights (it gives LSE), and
-        // w_run sums exactly the bf16 weights the PV MFMA uses, so that O =
-        // sum p'v / sum p' is a convex combination of V rows (bf16 rounding
-        // of a dominant weight then cancels instead of scaling O).
-        const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) l_run += x[kt][8 * a + u];
-        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), one2, w_run, false);
-        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), one2, w_run, false);
-        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), one2, w_run, false);
-        w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), one2, w_run, false);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8_t vv = *reinterpret_cast<const bf16x8_t*>(
-              vb + (dt * 32 + j) * VS + kt * 32 + 16 * a + 8 * h);
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb, oacc[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < NDT; ++dt) {
+        const char* base = vb + (vaddr0 ^ (64 * dt));
+        const int off = (32 * half + 16 * a) * RB;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + off));
+        const i16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + off + 4 * RB));
+        const bf16x8_t vv = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[a], oacc[dt], 0, 0, 0);
       }
   };
 
-  gload(0);
-  lstore(0);
+  // Online softmax of one 32-key score sub-tile x whose first key is key0
+  // ("FlashAttention -- avoid writing the giant intermediate", "Tiling and
+  // an incremental normalization"; "Attention Mechanism", section 3).
+  // Produces the bf16 weights pb, updates m_run, l_run, w_run and sets alpha
+  // to the factor the output accumulator must be multiplied by before pb is
+  // accumulated (1 for rows whose max did not move); returns whether any row
+  // of the wave has alpha != 1.
+  auto softmax = [&](f32x16_t& x, bf16x8_t(&pb)[2],
+                     float& alpha) __attribute__((always_inline)) -> bool {
+    // Row max over the sub-tile; the two lane halves holding a query's
+    // scores exchange theirs.
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+    const float mt = pair_max(mx) * cm;
+    // Raise a row's running max only when the sub-tile's max outgrows it by
+    // more than kLazyRescale (m = -inf on the first visible sub-tile always
+    // does).  The decision is per row, so a row's result never depends on
+    // other rows.
+    const bool grow = mt > m_run + kLazyRescale;
+    alpha = grow ? exp2_hw(m_run - mt) : 1.0f;  // exp2(-inf) = 0
+    m_run = grow ? mt : m_run;
+    l_run *= alpha;
+    w_run *= alpha;
+    // A row with no visible key so far keeps m = -inf; subtract 0 instead so
+    // that its terms are exp2(-inf) = 0 rather than NaN.
+    const float base = (m_run == -INFINITY) ? 0.0f : m_run;
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(x[r], cm, -base));
+    l_run += sum_tree<16>(p);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pb[a][u] = (__bf16)p[8 * a + u];
+      // w_run sums exactly the bf16 weights the PV MFMA uses, so that O =
+      // sum p'v / sum p' is a convex combination of V rows.
+      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 0, 1), one2,
+                                              w_run, false);
+      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 2, 3), one2,
+                                              w_run, false);
+      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 4, 5), one2,
+                                              w_run, false);
+      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 6, 7), one2,
+                                              w_run, false);
+    }
+    // Keep every softmax instruction in the MFMA block: without this the
+    // compiler may sink them past the rescale branch that follows.
+    asm volatile("" ::"v"(l_run), "v"(w_run), "v"(pb[0]), "v"(pb[1]));
+    return __builtin_amdgcn_ballot_w64(grow) != 0;
+  };
+
+  auto rescale = [&](float alpha) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+  };
+
+  // Interleave the block's MFMAs with its LDS reads and VALU work.
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (V^T)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    }
+  };
+
+  // Score tiles and bf16 weights of consecutive sub-tiles alternate between
+  // the X (even k) and Y (odd k) registers, so the pipeline never copies.
+  f32x16_t sX, sY;
+  bf16x8_t pX[2], pY[2];
+
+  // One sub-step for score sub-tile k: S_k is in scur, P_{k-1} in pprev;
+  // computes S_{k+1} from K half kh of kb and accumulates P_{k-1} V_{k-1}
+  // from V half vh of vb.
+  // Scale-then-mask of sub-tile k's scores (keys 32 k ..): keys past the
+  // end of the sequence and, when causal, keys after the query get -inf.
+  // Only sub-tiles k >= nfs need it.
+  auto mask = [&](f32x16_t& x, int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * k + acc_key_perm(r, h);
+      if (key >= T || (CAUSAL && key > qg)) x[r] = -INFINITY;
+    }
+  };
+  auto substep = [&](auto has_pv, const char* kb, int kh, const char* vb, int vh, f32x16_t& scur,
+                     f32x16_t& snext, const bf16x8_t(&pprev)[2], bf16x8_t(&pcur)[2],
+                     int k) __attribute__((always_inline)) {
+    if constexpr (PRESCALE) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) scur[r] *= c;
+    }
+    if (k >= nfs) mask(scur, k);
+    qk(kb, kh, snext);
+    if constexpr (decltype(has_pv)::value) pv(vb, vh, pprev);
+    float alpha;
+    const bool any = softmax(scur, pcur, alpha);
+    interleave();
+    if (any) rescale(alpha);
+  };
+
+  // Iteration tau: sub-steps k = 2 tau + 1 and 2 tau + 2.  K_{tau+1} and V_tau
+  // are in LDS (buffers (tau+1)&1 and tau&1); K_{tau+2} and V_{tau+1} are
+  // loaded into the buffers freed by the previous iteration.
+  auto iteration = [&](auto vbuf, int tau) __attribute__((always_inline)) {
+    constexpr int VB = decltype(vbuf)::value;  // tau & 1
+    char* kcur = VB ? sK0 : sK1;
+    char* kfree = VB ? sK1 : sK0;
+    char* vcur = VB ? sV1 : sV0;
+    char* vfree = VB ? sV0 : sV1;
+    if (tau + 2 < ntiles) dma_k(kfree, tau + 2);
+    if (tau + 1 < ntiles) dma_v(vfree, tau + 1);
+    substep(std::true_type{}, kcur, 0, vcur, 0, sY, sX, pX, pY, 2 * tau + 1);
+    substep(std::true_type{}, kcur, 1, vcur, 1, sX, sY, pY, pX, 2 * tau + 2);
+    // This wave's direct-to-LDS writes are complete; the barrier then makes
+    // every wave's writes visible and frees the buffers read here.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+  };
+
+  // Prologue: K_0, V_0 and K_1 into LDS, S_0, then sub-step 0 (no P V yet).
+  dma_k(sK0, 0);
+  dma_v(sV0, 0);
+  if (1 < ntiles) dma_k(sK1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  int t = 0;
-  for (; t < n_full; ++t) {
-    if (t + 1 < ntiles) gload(t + 1);
-    compute(t & 1, t * BC, std::false_type{});
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
-    __syncthreads();
-  }
-  for (; t < ntiles; ++t) {
-    if (t + 1 < ntiles) gload(t + 1);
-    const int kv0 = t * BC;
-    // Under a causal mask a wave skips tiles that start after its last query.
-    if (!CAUSAL || kv0 <= q0w + 31) compute(t & 1, kv0, std::true_type{});
-    if (t + 1 < ntiles) lstore((t + 1) & 1);
-    __syncthreads();
+  qk(sK0, 0, sX);
+  substep(std::false_type{}, sK0, 1, sV0, 0, sX, sY, pY, pX, 0);
+  // K_0's buffer receives K_2 in iteration 0: every wave must be done
+  // reading it first.
+  __syncthreads();
+
+  // Sub-tiles past the last tile's keys (k = 2 ntiles) are fully masked, so
+  // their softmax leaves the running state unchanged.
+  for (int tau = 0; tau < ntiles; tau += 2) {
+    iteration(std::integral_constant<int, 0>{}, tau);
+    if (tau + 1 >= ntiles) break;
+    iteration(std::integral_constant<int, 1>{}, tau + 1);
   }
 
   // Epilogue: combine the two lane halves' partial normalisers.
