@@ -28,6 +28,9 @@ HIPCC_FLAGS = [
     "-shared",
     # keep hipcc from emitting packed fp32 VALU ops (v_pk_fma/mul/add_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # device code only: no NaN inputs are supported, so float max needs no
+    # NaN-quieting (the host keeps IEEE semantics for argument validation)
+    "-Xarch_device", "-fno-honor-nans",
     "-Wall",
 ]
 

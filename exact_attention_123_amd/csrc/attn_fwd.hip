@@ -55,8 +55,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;  // 4 waves of 64 lanes
-constexpr int kBR = 128;       // query rows per workgroup (32 per wave)
+// fp32 kernel: 4 waves, 128 query rows per workgroup (32 per wave).
+constexpr int kThreads = 256;
+constexpr int kBR = 128;
+// bf16 kernel: 8 waves, 256 query rows per workgroup (32 per wave).
+constexpr int kThreadsBf16 = 512;
+constexpr int kBRBf16 = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -113,8 +117,13 @@ __device__ __forceinline__ float pair_max(float x) {
 // is only raised when a tile's max exceeds it by more than this, so p =
 // exp2(c*s - m) stays below 2^kLazyRescale and the output accumulator and
 // normaliser are rescaled only on those (rare, wave-uniform) occasions.  The
-// result is the same softmax: the common factor cancels in acc / l.
-constexpr float kLazyRescale = 8.0f;
+// result is the same softmax: the common factor cancels in acc / l.  With
+// 2^64 as the largest weight, the normaliser stays below 2^64 * T < 2^96 and
+// the accumulator below 2^96 * max|v|, far inside fp32 (and bf16) range, and
+// relative rounding is the same as with an exact max.  Weights more than
+// 2^126 below the stale max flush to zero; relative to the true max they are
+// smaller still, so they are negligible either way.
+constexpr float kLazyRescale = 64.0f;
 
 // Online-softmax update for one wave's tile of scores ("FlashAttention --
 // avoid writing the giant intermediate", "Tiling and an incremental
@@ -169,9 +178,9 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 template <int D>
 struct Bf16Tile {
+  static constexpr int NW = kThreadsBf16 / 64;  // waves per workgroup
   static constexpr int BC = 64;             // keys per tile
-  static constexpr int NKT = BC / 32;       // 32-key score tiles
-  static constexpr int NKC = BC / 16;       // 16-key steps of the PV MFMA
+  static constexpr int NST = 3;             // LDS stages per operand
   static constexpr int NDS = D / 16;        // 16-wide d steps of the QK MFMA
   static constexpr int NDT = D / 32;        // 32-row d tiles of O^T
   static constexpr int RB = D * 2;          // bytes per row of Q, K, V, O
@@ -182,16 +191,17 @@ struct Bf16Tile {
   static constexpr int KSLOT = NCH + 1;
   static constexpr int KROWB = KSLOT * 16;
   static constexpr int KBYTES = BC * KROWB;
-  static constexpr int KDMA = KBYTES / 1024;      // 1 KiB direct-to-LDS blocks
-  static constexpr int KPER = (KDMA + 3) / 4;     // blocks per wave (at most)
+  static constexpr int KDMA = KBYTES / 1024;       // 1 KiB direct-to-LDS blocks
+  static constexpr int KPER = (KDMA + NW - 1) / NW;  // load instructions per wave
   // V tile in LDS: unpadded rows with an XOR swizzle of the 16-byte chunks
   // (see v_chunk_swizzle), 1 KiB blocks of RPK rows.
   static constexpr int VBYTES = BC * RB;
   static constexpr int VDMA = VBYTES / 1024;
-  static constexpr int VPER = VDMA / 4;
+  static constexpr int VPER = VDMA / NW;
   static constexpr int RPK = 1024 / RB;
   static constexpr int RPB = 256 / RB;      // rows per 256-byte bank cycle
-  static_assert(KBYTES % 1024 == 0 && VBYTES % 4096 == 0, "tile split");
+  static_assert(KBYTES % 1024 == 0 && VDMA % NW == 0 && VPER <= 4, "tile split");
+  static_assert(NST * (KBYTES + VBYTES) <= 160 * 1024, "LDS");
 };
 
 // XOR applied to the 16-byte chunk index of V row r.  The transposing LDS
@@ -219,10 +229,11 @@ __device__ __forceinline__ float sum_tree(const float* x) {
   return (a + b) + (c + d);
 }
 
-// One wave owns 32 query rows; the workgroup (4 waves) 128 rows of one head.
-// Key/value tiles of 64 keys stream through LDS, written by direct-to-LDS
-// buffer loads (no staging registers) two tiles (K) and one tile (V) ahead
-// of their use.
+// One wave owns 32 query rows; the workgroup (8 waves) 256 rows of one head.
+// Key/value tiles of 64 keys stream through three LDS stages per operand,
+// written by direct-to-LDS buffer loads (no staging registers) three tiles
+// (K) and two tiles (V) ahead of their use, so a load has two tile periods
+// to land.
 //
 // The online softmax runs on score sub-tiles of 32 keys, software-pipelined
 // per wave: while the VALU computes the softmax of sub-tile k, the matrix
@@ -235,21 +246,27 @@ __device__ __forceinline__ float sum_tree(const float* x) {
 // otherwise (c > 0) the multiply is folded into the exponent's fma and the
 // max is taken over the raw scores.
 template <int D, bool CAUSAL, bool PRESCALE>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, float c) {
   using C = Bf16Tile<D>;
-  constexpr int BC = C::BC, NDS = C::NDS, NDT = C::NDT;
+  constexpr int NW = C::NW, BC = C::BC, NDS = C::NDS, NDT = C::NDT;
   constexpr int RB = C::RB, NCH = C::NCH, KSLOT = C::KSLOT, KROWB = C::KROWB;
   constexpr int KDMA = C::KDMA, KPER = C::KPER, VPER = C::VPER, RPK = C::RPK;
   static_assert(BC == 64, "two 32-key score sub-tiles per LDS tile");
 
-  // LDS: two K and two V buffers, separate objects so that the compiler can
-  // tell the direct-to-LDS writes into one buffer from reads of another.
+  // LDS: three K and three V stages, separate objects so that the compiler
+  // can tell the direct-to-LDS writes into one stage from reads of another.
   __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
   __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK2[C::KBYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV2[C::VBYTES];
+  // Target of the K load instructions of waves that have no K block left
+  // (KDMA is not a multiple of NW): every wave then issues the same number
+  // of loads per tile, which keeps the wait counts below exact.  Never read.
+  __shared__ __attribute__((aligned(1024))) char sSink[1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int head_bytes = T * RB;
   const __bf16* Kh = K + head;
   const __bf16* Vh = V + head;
-  const int q0 = qb * kBR;
+  const int q0 = qb * kBRBf16;
   const int qg = q0 + wave * 32 + j;
 
   // Q fragment: B operand of S^T = K Q^T; lane (j, h) holds
@@ -274,8 +291,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       qf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rQ, qg * RB + (16 * s + 8 * h) * 2));
   }
 
-  const int kv_end = CAUSAL ? min(T, q0 + kBR) : T;
+  const int kv_end = CAUSAL ? min(T, q0 + kBRBf16) : T;
   const int ntiles = (kv_end + BC - 1) / BC;
+  const int kv_bytes = kv_end * RB;
   // Score sub-tiles (32 keys) below nfs need no mask: every key is < T and,
   // when causal, no later than the workgroup's first query.
   const int nfs = (CAUSAL ? min(q0 + 1, T) : T) / 32;
@@ -284,13 +302,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // lane L's 16 bytes landing at block offset 16 L; each lane picks the
   // global chunk that belongs there.  K: block b holds padded slots
   // 64 b .. 64 b + 63 (slot u = row u / KSLOT, chunk u % KSLOT; the pad slot
-  // re-reads the row's last chunk).  Wave w writes blocks w, w + 4, ...
+  // re-reads the row's last chunk).  Wave w writes blocks w, w + NW, ...
   int koff[KPER];
 #pragma unroll
   for (int n = 0; n < KPER; ++n) {
-    const int u = 64 * (wave + 4 * n) + lane;
+    const int u = 64 * (wave + NW * n) + lane;
     const int r = u / KSLOT, ch = u % KSLOT;
-    koff[n] = r * RB + 16 * min(ch, NCH - 1);
+    koff[n] = r * RB + 16 * (ch < NCH ? ch : NCH - 1);
   }
   // V: wave w writes blocks VPER w .. VPER w + VPER - 1 (block b holds rows
   // RPK b .. RPK b + RPK - 1).
@@ -300,36 +318,57 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const int pc = lane % NCH;
     voff = r * RB + 16 * (pc ^ v_chunk_swizzle<D>(r));
   }
+  // Both are issued for every tile index, also past the last tile: keys at
+  // or past kv_end read as zero without touching memory (the descriptor's
+  // size ends there), so the count of loads per wave and tile is fixed.
   auto dma_k = [&](char* buf, int t) __attribute__((always_inline)) {
     const int kv0 = t * BC;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(Kh + (size_t)kv0 * D, max(head_bytes - kv0 * RB, 0));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * D, max(kv_bytes - kv0 * RB, 0));
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(Kh, 0);
 #pragma unroll
     for (int n = 0; n < KPER; ++n) {
       // (a plain local: host-side template instantiation drops the kernel
       // when an array element is passed to this builtin directly)
       const int off = koff[n];
-      if (wave + 4 * n < KDMA)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + 1024 * (wave + 4 * n)), 16,
-                                                 off, 0, 0, 0);
+      const bool real = wave + NW * n < KDMA;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          real ? r : none, (lds_void_t*)(real ? buf + 1024 * (wave + NW * n) : sSink), 16, off,
+          0, 0, 0);
     }
   };
   auto dma_v = [&](char* buf, int t) __attribute__((always_inline)) {
     const int kv0 = t * BC;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(Vh + (size_t)kv0 * D, max(head_bytes - kv0 * RB, 0));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Vh + (size_t)kv0 * D, max(kv_bytes - kv0 * RB, 0));
     // The instruction offset (1024 n) advances both the global and the LDS
     // address; voffset only moves the global one.
     lds_void_t* dst = (lds_void_t*)(buf + 1024 * VPER * wave);
     auto block = [&](auto n) __attribute__((always_inline)) {
       constexpr int N = decltype(n)::value;
-      if constexpr (N < VPER) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 1024 * N, 0);
+      if constexpr (N < VPER)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 1024 * N, 0);
     };
-    static_assert(VPER <= 4, "V blocks per wave");
     block(std::integral_constant<int, 0>{});
     block(std::integral_constant<int, 1>{});
     block(std::integral_constant<int, 2>{});
     block(std::integral_constant<int, 3>{});
+  };
+  // Workgroup barrier for the LDS stages.  __syncthreads() would also wait
+  // for every load in flight, including the direct-to-LDS loads of the next
+  // stages; this waits only for this wave's LDS reads (lgkmcnt) and keeps the
+  // compiler from moving memory accesses across it.  The stage loads that
+  // must have landed are waited for explicitly (wait_dma) before it.
+  auto stage_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Waits until at most n of this wave's direct-to-LDS loads are still in
+  // flight (they complete in issue order).
+  auto wait_dma = [&](auto n) __attribute__((always_inline)) {
+    constexpr int N = decltype(n)::value;
+    static_assert(N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
   };
 
   // LDS read addresses.  K (A operand of the QK MFMA): lane (j, h) reads row
@@ -343,18 +382,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // + i] for e = 0..3: four consecutive keys of one d, i.e. V^T.  The
   // swizzle only flips chunk bits 2-3, i.e. the dt field, so the address of
   // tile dt is vaddr0 ^ (64 dt).
-  int vaddr0;
+  int vaddr[NDT];
   {
     const int g = lane >> 4, l = lane & 15;
     const int r = 8 * (g >> 1) + (l >> 2);
     const int ch = 2 * (g & 1) + ((l >> 1) & 1);
-    vaddr0 = r * RB + 16 * (ch ^ v_chunk_swizzle<D>(r)) + 8 * (l & 1);
+    const int vaddr0 = r * RB + 16 * (ch ^ v_chunk_swizzle<D>(r)) + 8 * (l & 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vaddr[dt] = vaddr0 ^ (64 * dt);
   }
 
   f32x16_t oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.0f, w_run = 0.0f;
+  // The running max starts at a finite value far below any score in log2
+  // units (|scores| <= 2^127 * |c|): the first visible sub-tile always
+  // raises it (alpha = exp2(-huge) = 0), and masked scores (-inf) still give
+  // weight exp2(-inf) = 0.
+  constexpr float kMinusHuge = -1e38f;
+  float m_run = kMinusHuge, l_run = 0.0f, w_run = 0.0f;
   const float cm = PRESCALE ? 1.0f : c;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -376,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const char* base = vb + (vaddr0 ^ (64 * dt));
+        const char* base = vb + vaddr[dt];
         const int off = (32 * half + 16 * a) * RB;
         const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + off));
         const i16x4_t hi =
@@ -387,13 +433,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       }
   };
 
-  // Online softmax of one 32-key score sub-tile x whose first key is key0
-  // ("FlashAttention -- avoid writing the giant intermediate", "Tiling and
-  // an incremental normalization"; "Attention Mechanism", section 3).
-  // Produces the bf16 weights pb, updates m_run, l_run, w_run and sets alpha
-  // to the factor the output accumulator must be multiplied by before pb is
-  // accumulated (1 for rows whose max did not move); returns whether any row
-  // of the wave has alpha != 1.
+  // Online softmax of one 32-key score sub-tile x ("FlashAttention -- avoid
+  // writing the giant intermediate", "Tiling and an incremental
+  // normalization"; "Attention Mechanism", section 3).  Produces the bf16
+  // weights pb, updates m_run, l_run, w_run and sets alpha to the factor the
+  // output accumulator must be multiplied by before pb is accumulated (1 for
+  // rows whose max did not move); returns whether any row of the wave has
+  // alpha != 1.
   auto softmax = [&](f32x16_t& x, bf16x8_t(&pb)[2],
                      float& alpha) __attribute__((always_inline)) -> bool {
     // Row max over the sub-tile; the two lane halves holding a query's
@@ -407,16 +453,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     // does).  The decision is per row, so a row's result never depends on
     // other rows.
     const bool grow = mt > m_run + kLazyRescale;
-    alpha = grow ? exp2_hw(m_run - mt) : 1.0f;  // exp2(-inf) = 0
+    alpha = grow ? exp2_hw(m_run - mt) : 1.0f;
     m_run = grow ? mt : m_run;
     l_run *= alpha;
     w_run *= alpha;
-    // A row with no visible key so far keeps m = -inf; subtract 0 instead so
-    // that its terms are exp2(-inf) = 0 rather than NaN.
-    const float base = (m_run == -INFINITY) ? 0.0f : m_run;
     float p[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(x[r], cm, -base));
+    for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(x[r], cm, -m_run));
     l_run += sum_tree<16>(p);
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
@@ -446,16 +489,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
   };
 
-  // Interleave the block's MFMAs with its LDS reads and VALU work.
+  // Interleave the block's MFMAs with its LDS reads and VALU work; the LDS
+  // reads run a few MFMAs ahead of their use so that their latency is hidden.
   auto interleave = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads ahead
 #pragma unroll
-    for (int i = 0; i < NDS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K)
+    for (int i = 0; i < 2 * NDS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (V^T)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+    }
+  };
+
+  // Scale-then-mask of sub-tile k's scores (keys 32 k ..): keys past the end
+  // of the sequence and, when causal, keys after the query get -inf.  Only
+  // sub-tiles k >= nfs need it.
+  auto mask = [&](f32x16_t& x, int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * k + acc_key_perm(r, h);
+      if (key >= T || (CAUSAL && key > qg)) x[r] = -INFINITY;
     }
   };
 
@@ -467,16 +520,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // One sub-step for score sub-tile k: S_k is in scur, P_{k-1} in pprev;
   // computes S_{k+1} from K half kh of kb and accumulates P_{k-1} V_{k-1}
   // from V half vh of vb.
-  // Scale-then-mask of sub-tile k's scores (keys 32 k ..): keys past the
-  // end of the sequence and, when causal, keys after the query get -inf.
-  // Only sub-tiles k >= nfs need it.
-  auto mask = [&](f32x16_t& x, int k) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 32 * k + acc_key_perm(r, h);
-      if (key >= T || (CAUSAL && key > qg)) x[r] = -INFINITY;
-    }
-  };
   auto substep = [&](auto has_pv, const char* kb, int kh, const char* vb, int vh, f32x16_t& scur,
                      f32x16_t& snext, const bf16x8_t(&pprev)[2], bf16x8_t(&pcur)[2],
                      int k) __attribute__((always_inline)) {
@@ -494,42 +537,50 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   };
 
   // Iteration tau: sub-steps k = 2 tau + 1 and 2 tau + 2.  K_{tau+1} and V_tau
-  // are in LDS (buffers (tau+1)&1 and tau&1); K_{tau+2} and V_{tau+1} are
-  // loaded into the buffers freed by the previous iteration.
-  auto iteration = [&](auto vbuf, int tau) __attribute__((always_inline)) {
-    constexpr int VB = decltype(vbuf)::value;  // tau & 1
-    char* kcur = VB ? sK0 : sK1;
-    char* kfree = VB ? sK1 : sK0;
-    char* vcur = VB ? sV1 : sV0;
-    char* vfree = VB ? sV0 : sV1;
-    if (tau + 2 < ntiles) dma_k(kfree, tau + 2);
-    if (tau + 1 < ntiles) dma_v(vfree, tau + 1);
+  // are in LDS (stages (tau+1)%3 and tau%3); K_{tau+3} and V_{tau+2} are
+  // loaded into the stages freed by the previous iteration.  At the end the
+  // loads of the previous iteration (K_{tau+2}, V_{tau+1}) must have landed.
+  auto iteration = [&](auto stage, int tau) __attribute__((always_inline)) {
+    constexpr int R = decltype(stage)::value;  // tau % 3
+    char* kcur = R == 0 ? sK1 : R == 1 ? sK2 : sK0;
+    char* kfree = R == 0 ? sK0 : R == 1 ? sK1 : sK2;
+    char* vcur = R == 0 ? sV0 : R == 1 ? sV1 : sV2;
+    char* vfree = R == 0 ? sV2 : R == 1 ? sV0 : sV1;
+    dma_k(kfree, tau + 3);
+    dma_v(vfree, tau + 2);
     substep(std::true_type{}, kcur, 0, vcur, 0, sY, sX, pX, pY, 2 * tau + 1);
     substep(std::true_type{}, kcur, 1, vcur, 1, sX, sY, pY, pX, 2 * tau + 2);
-    // This wave's direct-to-LDS writes are complete; the barrier then makes
-    // every wave's writes visible and frees the buffers read here.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
+    // Every wave issued KPER + VPER loads this iteration: waiting down to
+    // that many in flight means K_{tau+2} and V_{tau+1} have landed.
+    wait_dma(std::integral_constant<int, KPER + VPER>{});
+    // The barrier makes every wave's landed writes visible and frees the
+    // stages read in this iteration.
+    stage_barrier();
   };
 
-  // Prologue: K_0, V_0 and K_1 into LDS, S_0, then sub-step 0 (no P V yet).
+  // Prologue: K_0, V_0, K_1, V_1, K_2 into LDS, S_0, then sub-step 0 (no
+  // P V yet).
   dma_k(sK0, 0);
   dma_v(sV0, 0);
-  if (1 < ntiles) dma_k(sK1, 1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  dma_k(sK1, 1);
+  dma_v(sV1, 1);
+  dma_k(sK2, 2);
+  wait_dma(std::integral_constant<int, 0>{});
   __syncthreads();
   qk(sK0, 0, sX);
   substep(std::false_type{}, sK0, 1, sV0, 0, sX, sY, pY, pX, 0);
-  // K_0's buffer receives K_2 in iteration 0: every wave must be done
+  // K_0's stage receives K_3 in iteration 0: every wave must be done
   // reading it first.
   __syncthreads();
 
   // Sub-tiles past the last tile's keys (k = 2 ntiles) are fully masked, so
   // their softmax leaves the running state unchanged.
-  for (int tau = 0; tau < ntiles; tau += 2) {
+  for (int tau = 0; tau < ntiles; tau += 3) {
     iteration(std::integral_constant<int, 0>{}, tau);
     if (tau + 1 >= ntiles) break;
     iteration(std::integral_constant<int, 1>{}, tau + 1);
+    if (tau + 2 >= ntiles) break;
+    iteration(std::integral_constant<int, 2>{}, tau + 2);
   }
 
   // Epilogue: combine the two lane halves' partial normalisers.
@@ -753,14 +804,17 @@ attn_status check_device() {
   return s == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
+// Launches one workgroup of `threads` threads per `rows` query rows of each
+// head.
 template <typename Elem>
-attn_status launch(const void* kernel, const Elem* q, const Elem* k, const Elem* v, Elem* o,
-                   float* lse, int64_t B, int64_t H, int64_t T, float scale, hipStream_t stream) {
-  int t = (int)T, bh = (int)(B * H), nqb = (int)((T + kBR - 1) / kBR);
+attn_status launch(const void* kernel, int threads, int rows, const Elem* q, const Elem* k,
+                   const Elem* v, Elem* o, float* lse, int64_t B, int64_t H, int64_t T,
+                   float scale, hipStream_t stream) {
+  int t = (int)T, bh = (int)(B * H), nqb = (int)((T + rows - 1) / rows);
   float c = scale * kLog2e;
   void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
                   (void*)&t, (void*)&bh,  (void*)&nqb, (void*)&c};
-  const dim3 grid((unsigned)(bh * nqb)), block(kThreads);
+  const dim3 grid((unsigned)(bh * nqb)), block(threads);
   if (hipLaunchKernel(kernel, grid, block, args, 0, stream) != hipSuccess) return ATTN_ERR_LAUNCH;
   return ATTN_OK;
 }
@@ -795,8 +849,9 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   attn_status st = validate(q, k, v, o, lse, B, H, T, d, causal, scale, 2, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  return launch<__bf16>(bf16_kernel(d, causal, scale), (const __bf16*)q, (const __bf16*)k,
-                        (const __bf16*)v, (__bf16*)o, lse, B, H, T, scale, stream);
+  return launch<__bf16>(bf16_kernel(d, causal, scale), kThreadsBf16, kBRBf16, (const __bf16*)q,
+                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, B, H, T, scale,
+                        stream);
 }
 
 attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -806,7 +861,8 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* 
   attn_status st = validate(q, k, v, o, lse, B, H, T, d, causal, scale, 4, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  return launch<float>(f32_kernel(d, causal), q, k, v, o, lse, B, H, T, scale, stream);
+  return launch<float>(f32_kernel(d, causal), kThreads, kBR, q, k, v, o, lse, B, H, T, scale,
+                       stream);
 }
 
 const char* attn_status_string(attn_status s) {
@@ -828,8 +884,8 @@ const char* attn_kernel_name(int is_f32, int64_t d, int causal) {
   if (d != 64 && d != 128) return nullptr;
   if (causal != 0 && causal != 1) return nullptr;
   static const char* names[2][2][2] = {
-      {{"attn_fwd_bf16_d64_full_br128_bc64_w4", "attn_fwd_bf16_d64_causal_br128_bc64_w4"},
-       {"attn_fwd_bf16_d128_full_br128_bc64_w4", "attn_fwd_bf16_d128_causal_br128_bc64_w4"}},
+      {{"attn_fwd_bf16_d64_full_br256_bc64_w8", "attn_fwd_bf16_d64_causal_br256_bc64_w8"},
+       {"attn_fwd_bf16_d128_full_br256_bc64_w8", "attn_fwd_bf16_d128_causal_br256_bc64_w8"}},
       {{"attn_fwd_f32_d64_full_br128_bc32_w4", "attn_fwd_f32_d64_causal_br128_bc32_w4"},
        {"attn_fwd_f32_d128_full_br128_bc32_w4", "attn_fwd_f32_d128_causal_br128_bc32_w4"}}};
   return names[is_f32 ? 1 : 0][d == 128 ? 1 : 0][causal];

@@ -97,7 +97,7 @@ const char* attn_status_string(attn_status s);
 /*
  * Name of the kernel instance attn_fwd (is_f32 = 0) or attn_fwd_f32
  * (is_f32 = 1) launches for head dimension d and the causal flag, e.g.
- * "attn_fwd_bf16_d128_causal_br128_bc64_w4", so that a caller can log which
+ * "attn_fwd_bf16_d128_causal_br256_bc64_w8", so that a caller can log which
  * kernel ran.  NULL if the combination is unsupported.
  */
 const char* attn_kernel_name(int is_f32, int64_t d, int causal);
