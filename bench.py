@@ -16,7 +16,6 @@ timed on a bounded sample of the same workload on this host's cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -31,26 +30,24 @@ METRIC = "fused causal attn fwd TFLOP/s (bf16, T=8192, d=128) + % MFMA peak"
 DEFAULT_WORKLOAD = "bf16_b1h32_t8192_d128_causal_qk4"
 # MI355X published dense peaks (TFLOP/s) by MFMA input type.
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_123_amd", "csrc", "attn_fwd.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this kernel and workload, or None when there is none or the kernel source
-    changed since the counters were taken."""
+    code changed since the counters were taken."""
+    from exact_attention_123_amd.rocprof_summary import source_sha
+
     path = os.path.join(PROFILES, f"{kernel}__{workload}__traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    h = re.search(r"kernel_code_sha256:\s*([0-9a-f]+)", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not h or not b or h.group(1) != kernel_source_hash():
+    if not h or not b or h.group(1) != source_sha():
         return None
     return float(b.group(1))
 
@@ -91,8 +88,8 @@ def cpu_baseline(x, causal: bool, scale: float, heads: int):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32,

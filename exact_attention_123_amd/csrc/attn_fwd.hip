@@ -12,8 +12,9 @@
 // tiles in registers, so no T x T array touches HBM ("Attention Mechanism",
 // sections 3-4: tiling, fusion, online softmax).  Each key/value tile is
 // loaded once per workgroup from global memory with 16-byte coalesced loads
-// into LDS (double-buffered: the loads of tile t+1 are in flight while
-// tile t is computed) and read from LDS by all waves of the workgroup.
+// into LDS, ahead of its use (bf16: three stages, direct-to-LDS; fp32: two
+// stages through registers), and read from LDS by all waves of the
+// workgroup.
 //
 // Per wave (32 query rows), per tile of BC keys:
 //   1. S^T = K Q^T on MFMA 32x32x16 bf16 (fp32 accumulate).  Computing the

@@ -8,6 +8,12 @@ Two summaries per (kernel, workload):
     ``rocprofv3 --kernel-trace --stats`` run of ``bench.py``, and the
     TFLOP/s that average implies.
 
+``<kernel>__<workload>__mfma_util.md``
+    matrix-core busy fraction from one ``rocprofv3 --pmc`` run of
+    ``SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA``:
+    busy SIMD-cycles over (GPU-active cycles per XCD x 1024 SIMDs), and the
+    clock that GPU-active cycles over the traced average duration imply.
+
 ``<kernel>__<workload>__traffic.md``
     device-memory bytes per launch from two ``rocprofv3 --pmc`` runs
     (``FETCH_SIZE``, then ``WRITE_SIZE``), each scaled by what the same
@@ -30,6 +36,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -40,9 +47,21 @@ KERNEL_MARK = "attn_fwd_"  # substring of every attention kernel's symbol
 COPY_MARK = "copyBuffer"   # the runtime's device-to-device copy kernel
 
 
+def code_sha(text: str) -> str:
+    """SHA-256 (first 16 hex digits) of kernel source text with its ``//``
+    comments and blank lines removed: a summary stays valid across edits of
+    comments, and any change of code invalidates it."""
+    lines = []
+    for line in text.splitlines():
+        code = re.sub(r"//.*", "", line).rstrip()
+        if code.strip():
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(KERNEL_SRC) as f:
+        return code_sha(f.read())
 
 
 def _rows(path):
@@ -74,6 +93,15 @@ def counter_per_dispatch(path: str, counter: str):
     return statistics.mean(att), len(att), copy[-1]
 
 
+def counters_mean(path: str):
+    """{counter: mean value per attention dispatch} of a counter CSV."""
+    agg = {}
+    for r in _rows(path):
+        if KERNEL_MARK in r["Kernel_Name"]:
+            agg.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.mean(v) for k, v in agg.items()}, max(len(v) for v in agg.values())
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -88,6 +116,8 @@ def main() -> int:
     ap.add_argument("--kt-cmd", default="")
     ap.add_argument("--fetch-cmd", default="")
     ap.add_argument("--write-cmd", default="")
+    ap.add_argument("--util", help="counter CSV of the MFMA utilisation pass")
+    ap.add_argument("--util-cmd", default="")
     ap.add_argument("--out", default=PROFILES)
     a = ap.parse_args()
     os.makedirs(a.out, exist_ok=True)
@@ -99,12 +129,31 @@ def main() -> int:
         with open(base + "__kernel_trace.md", "w") as f:
             f.write(f"# {a.kernel} on {a.workload}: rocprofv3 kernel trace\n\n"
                     f"command: `{a.kt_cmd}`\n\n"
-                    f"kernel_source_sha256: {sha}\n\n"
+                    f"kernel_code_sha256: {sha}\n\n"
                     f"| symbol | calls | avg us | min us | max us | TFLOP/s at avg |\n"
                     f"|---|---|---|---|---|---|\n"
                     f"| `{sym}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | "
                     f"{mx / 1e3:.1f} | {a.flops / (avg * 1e-9) / 1e12:.1f} |\n")
         print("wrote", base + "__kernel_trace.md")
+
+    if a.util:
+        m, n = counters_mean(a.util)
+        xcd_cycles = m["GRBM_GUI_ACTIVE"] / 8  # the counter sums the 8 XCDs
+        util = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 1024)
+        other = (m["SQ_INSTS_VALU"] - m["SQ_INSTS_MFMA"]) / m["SQ_INSTS_MFMA"]
+        clock = ""
+        if a.stats:
+            clock = (f"clock implied by GPU-active cycles over the traced average duration: "
+                     f"{xcd_cycles / avg:.2f} GHz\n\n")
+        with open(base + "__mfma_util.md", "w") as f:
+            f.write(f"# {a.kernel} on {a.workload}: matrix-core utilisation\n\n"
+                    f"command: `{a.util_cmd}`\n\n"
+                    f"kernel_code_sha256: {sha}\n\n"
+                    f"| counter | mean per dispatch ({n}) |\n|---|---|\n"
+                    + "".join(f"| {k} | {v:.6g} |\n" for k, v in sorted(m.items()))
+                    + f"\nMFMA busy fraction: {util:.3f}\n\n"
+                    f"non-MFMA VALU instructions per MFMA: {other:.2f}\n\n" + clock)
+        print("wrote", base + "__mfma_util.md")
 
     if a.fetch and a.write:
         copy_bytes = a.copy_mib * (1 << 20)
@@ -117,7 +166,7 @@ def main() -> int:
             f.write(f"# {a.kernel} on {a.workload}: device-memory traffic per launch\n\n"
                     f"fetch command: `{a.fetch_cmd}`\n\n"
                     f"write command: `{a.write_cmd}`\n\n"
-                    f"kernel_source_sha256: {sha}\n\n"
+                    f"kernel_code_sha256: {sha}\n\n"
                     f"| counter | KiB per dispatch (mean of {fn}/{wn}) | copy of {a.copy_mib} "
                     f"MiB reads as KiB | scale | bytes per launch |\n|---|---|---|---|---|\n"
                     f"| FETCH_SIZE | {fk:.1f} | {fcopy:.1f} | {ff:.3f} | {fb:.4g} |\n"
