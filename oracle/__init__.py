@@ -10,6 +10,9 @@ attention arithmetic.
 Contents
   attention        -- materialised definition (scores, mask, row softmax, PV,
                       log-sum-exp); pinned by tests/test_oracle_pins.py.
+  backward         -- gradients dQ, dK, dV (and Delta) of the materialised
+                      definition for an upstream gradient dO; pinned by
+                      tests/test_oracle_bwd_pins.py.
   online_model     -- a float64 model of the tiled recurrence with running
                       max, running normaliser and rescaled accumulator, plus
                       the per-tile-normalisation negative control.  It is not
@@ -26,4 +29,5 @@ least one test that checks it against a value the pages print, a closed form,
 an invariant or an independent brute force.
 """
 from .attention import attention, attention_head, attention_heads  # noqa: F401
+from .backward import attention_head_bwd  # noqa: F401
 from .online_model import online_attention_head, tile_local_softmax_head  # noqa: F401
