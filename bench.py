@@ -1,17 +1,24 @@
 #!/usr/bin/env python3
-"""Benchmark of the fused exact-attention forward on one MI355X.
+"""Benchmark of the fused exact-attention passes on one MI355X.
 
-One step = one launch of the fused forward over the whole batch (every head,
-every query row): the entire hot path.  Default workload: B=1, H=32,
-T=8192, d=128, bf16, causal, Q and K drawn N(0,1) times 4 (scaled-score
-spread of 16), scale 1/sqrt(128).
+Default (``--pass fwd``): one step = one launch of the fused forward over the
+whole batch (every head, every query row): the entire hot path.  Default
+workload: B=1, H=32, T=8192, d=128, bf16, causal, Q and K drawn N(0,1) times 4
+(scaled-score spread of 16), scale 1/sqrt(128).  FLOPs counted: 4*T*T*d per
+head, halved under the causal mask.
 
-Prints one JSON line with the throughput (TFLOP/s, counting 4*T*T*d FLOPs
-per head, halved under the causal mask), the roofline position of the kernel
-(MFMA-bound, against MI355X's dense bf16 peak) and the float64 CPU oracle
-timed on a bounded sample of the same workload on this host's cores.
+``--pass bwd``: one step = one call of the backward (row statistics, dK/dV,
+dQ kernels) on the same workload with a seeded upstream gradient dO, after
+one untimed forward that provides O and LSE.  FLOPs counted: the five T x T x
+d contractions of the gradient, 2.5 times the forward's count.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+Prints one JSON line with the throughput, the roofline position of the pass
+(MFMA-bound, against MI355X's dense bf16 peak; for the backward the three
+kernels of one call are timed together) and the float64 CPU oracle timed on a
+bounded sample of the same workload on this host's cores.
+
+    python bench.py [--pass fwd|bwd] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -26,60 +33,73 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "fused causal attn fwd TFLOP/s (bf16, T=8192, d=128) + % MFMA peak"
 DEFAULT_WORKLOAD = "bf16_b1h32_t8192_d128_causal_qk4"
 # MI355X published dense peaks (TFLOP/s) by MFMA input type.
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PROFILES = os.path.join(ROOT, "profiles")
+DOUT_SEED_OFFSET = 7000  # dO seed = workload seed + this
 
 
+def metric_name(pass_: str, causal: bool, dt: str, T: int, d: int) -> str:
+    return (f"fused {'causal ' if causal else ''}attn {pass_} TFLOP/s ({dt}, T={T}, d={d}) "
+            f"+ % MFMA peak")
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary of
-    this kernel and workload, or None when there is none or the kernel source
+def measured_traffic(name: str, workload: str, pass_: str = "fwd"):
+    """HBM bytes per call from the committed rocprofv3 counter summary of
+    this pass and workload, or None when there is none or the pass's kernel
     code changed since the counters were taken."""
     from exact_attention_123_amd.rocprof_summary import source_sha
 
-    path = os.path.join(PROFILES, f"{kernel}__{workload}__traffic.md")
+    path = os.path.join(PROFILES, f"{name}__{workload}__traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     h = re.search(r"kernel_code_sha256:\s*([0-9a-f]+)", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not h or not b or h.group(1) != source_sha():
+    if not h or not b or h.group(1) != source_sha(pass_):
         return None
     return float(b.group(1))
 
 
-def cpu_baseline(x, causal: bool, scale: float, heads: int):
-    """Time the float64 oracle on the first `heads` heads (all rows)."""
-    import numpy as np
-
-    import oracle
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
         blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
-        threads = max((p["num_threads"] for p in blas), default=1)
+        return int(max((p["num_threads"] for p in blas), default=1))
     except Exception:  # pragma: no cover
-        threads = 1
+        return 1
+
+
+def cpu_baseline(x, causal: bool, scale: float, heads: int, pass_: str, do_bits=None):
+    """Time the float64 oracle on the first `heads` heads (all rows)."""
+    import oracle
+    from seeded_inputs import bf16_bits_to_f32
+
     B, H, T, d = x.shape
     t0 = time.perf_counter()
     done = 0
     for i in range(heads):
         b, h = divmod(i, H)
-        oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h), causal=causal,
-                              scale=scale)
+        if pass_ == "fwd":
+            oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h), causal=causal,
+                                  scale=scale)
+        else:
+            g = bf16_bits_to_f32(do_bits[b, h]).astype("float64")
+            oracle.attention_head_bwd(x.q64(b, h), x.k64(b, h), x.v64(b, h), g,
+                                      causal=causal, scale=scale)
         done += 1
     dt = time.perf_counter() - t0
-    fl = 4.0 * T * T * d * done / (2 if causal else 1)
+    fl = 4.0 * T * T * d * done / (2 if causal else 1) * (2.5 if pass_ == "bwd" else 1.0)
+    what = ("S and P materialised" if pass_ == "fwd"
+            else "forward, P, dP and dS materialised, all of dQ, dK, dV")
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": blas_threads(),
         "kind": "oracle",
-        "sample": f"{done} of {B * H} heads, all {T} query rows each; float64 numpy, "
-                  f"S and P materialised; {dt:.1f} s wall",
+        "sample": f"{done} of {B * H} heads, all {T} rows each; float64 numpy, {what}; "
+                  f"{dt:.1f} s wall",
         "seconds": dt,
         "host_cpus": len(os.sched_getaffinity(0)),
     }
@@ -90,10 +110,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32,
-                    help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-heads", type=int, default=None,
+                    help="heads of the workload the CPU oracle is timed on "
+                         "(default 32 for fwd, 2 for bwd)")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (for counter calibration)")
@@ -110,11 +132,15 @@ def main() -> int:
     import torch
 
     import exact_attention_123_amd as ea
-    from seeded_inputs import WORKLOADS, bf16_bits_to_f32, make_workload
+    from seeded_inputs import WORKLOADS, bf16_bits_to_f32, make_dout, make_workload
 
     w = WORKLOADS[args.workload]
     causal = w["causal"][0]
     B, H, T, d, dt = w["B"], w["H"], w["T"], w["d"], w["dtype"]
+    bwd = args.pass_ == "bwd"
+    if bwd and dt != "bf16":
+        print("the backward pass is bf16 only", file=sys.stderr)
+        return 2
     scale = 1.0 / math.sqrt(d)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -126,48 +152,83 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
+    def to64(t):
+        if dt == "bf16":
+            return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
+        return t.cpu().numpy()
+
     q, k, v = up(x.q), up(x.k), up(x.v)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-    kname = ea.kernel_name(dt == "f32", d, causal)
-    fl = ea.flops(B, H, T, d, causal)
+    if bwd:
+        do_bits = make_dout(B, H, T, d, seed=x.seed + DOUT_SEED_OFFSET)
+        dout = up(do_bits)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(2 * B * H * T, dtype=torch.float32, device=dev)
+        ea.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
+        kname = ea.bwd_kernel_name(d, causal, 1)
+        knames = [ea.bwd_kernel_name(d, causal, i) for i in range(3)]
+        fl = ea.bwd_flops(B, H, T, d, causal)
+    else:
+        do_bits = None
+        kname = ea.kernel_name(dt == "f32", d, causal)
+        knames = [kname]
+        fl = ea.flops(B, H, T, d, causal)
 
-    # Parity before timing: sampled rows of two heads against the oracle.
+    def step():
+        if bwd:
+            ea.backward(q, k, v, out, lse, dout, causal=causal, scale=scale, dq=dq, dk=dk,
+                        dv=dv, ws=ws)
+        else:
+            ea.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
+
+    # Parity before timing: sampled rows (and keys) of two heads against the
+    # oracle.
     parity = None
     if not args.no_parity:
         import oracle
-        ea.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
+        step()
         torch.cuda.synchronize()
-        if dt == "bf16":
-            O = bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16))
+        rng = np.random.Generator(np.random.PCG64(9))
+        rows = np.unique(np.r_[0, 1, 63, 64, 127, 128, T // 2, T - 1, rng.choice(T, 24)])
+        heads = ((0, 0), (B - 1, H - 1))
+        if not bwd:
+            O, L = to64(out), lse.cpu().numpy()
+            eo = el = 0.0
+            for (b, h) in heads:
+                ref = oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h),
+                                            causal=causal, scale=scale, rows=rows)
+                eo = max(eo, float(np.abs(O[b, h][rows] - ref["O"]).max()))
+                el = max(el, float(np.abs(L[b, h][rows] - ref["LSE"]).max()))
+            tol = (2e-2, 1e-3) if dt == "bf16" else (1e-5, 1e-5)
+            parity = {"rows_checked": int(2 * len(rows)), "max_abs_err_o": eo,
+                      "max_abs_err_lse": el, "pass": bool(eo <= tol[0] and el <= tol[1])}
         else:
-            O = out.cpu().numpy()
-        L = lse.cpu().numpy()
-        rows = np.unique(np.r_[0, 1, 63, 64, 127, 128, T // 2, T - 1,
-                               np.random.Generator(np.random.PCG64(9)).choice(T, 24)])
-        eo = el = 0.0
-        for (b, h) in ((0, 0), (B - 1, H - 1)):
-            ref = oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h),
-                                        causal=causal, scale=scale, rows=rows)
-            eo = max(eo, float(np.abs(O[b, h][rows] - ref["O"]).max()))
-            el = max(el, float(np.abs(L[b, h][rows] - ref["LSE"]).max()))
-        tol = (2e-2, 1e-3) if dt == "bf16" else (1e-5, 1e-5)
-        parity = {"rows_checked": int(2 * len(rows)), "max_abs_err_o": eo,
-                  "max_abs_err_lse": el, "pass": bool(eo <= tol[0] and el <= tol[1])}
+            # Relative to the largest reference magnitude of each gradient;
+            # the parity tests hold the per-element bound.
+            G = [to64(t) for t in (dq, dk, dv)]
+            worst = 0.0
+            for (b, h) in heads:
+                g = bf16_bits_to_f32(do_bits[b, h]).astype(np.float64)
+                ref = oracle.attention_head_bwd(x.q64(b, h), x.k64(b, h), x.v64(b, h), g,
+                                                causal=causal, scale=scale, rows=rows,
+                                                keys=rows)
+                for got, want in ((G[0][b, h][rows], ref["dQ"]), (G[1][b, h][rows], ref["dK"]),
+                                  (G[2][b, h][rows], ref["dV"])):
+                    worst = max(worst, float(np.abs(got - want).max() / np.abs(want).max()))
+            parity = {"rows_checked": int(2 * len(rows)), "keys_checked": int(2 * len(rows)),
+                      "max_err_rel_to_max_ref": worst, "pass": bool(worst <= 2e-2)}
         if not parity["pass"]:
             print(json.dumps({"error": "parity failed", "parity": parity}), flush=True)
             return 1
 
-    stream = torch.cuda.current_stream(dev)  # the launch stream of ea.forward
-
-    def step():
-        ea.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
+    stream = torch.cuda.current_stream(dev)  # the launch stream of the binding
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: events on the launch stream around each launch.
+    # Timed region: events on the launch stream around each call.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -193,10 +254,16 @@ def main() -> int:
     value = fl / (ms_per_step * 1e-3) / 1e12
     achieved = fl / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dt]
-    traffic = measured_traffic(kname, args.workload)
+    traffic = measured_traffic(kname, args.workload, args.pass_)
 
+    config = {"workload": args.workload, "pass": args.pass_, "B": B, "H": H, "T": T, "d": d,
+              "causal": causal, "scale": scale, "qk_mult": w.get("qk_mult", 1.0),
+              "flops_per_step": fl, "kernel": kname, "parallelism": "single GPU"}
+    if bwd:
+        config["kernels"] = knames
+        config["dout_seed"] = x.seed + DOUT_SEED_OFFSET
     res = {
-        "metric": METRIC,
+        "metric": metric_name(args.pass_, causal, dt, T, d),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -208,10 +275,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic: seeded PCG64 N(0,1) draws rounded to bf16 (RNE)"
-                + (", Q and K multiplied by 4" if w.get("qk_mult", 1.0) != 1.0 else ""),
-        "config": {"workload": args.workload, "B": B, "H": H, "T": T, "d": d,
-                   "causal": causal, "scale": scale, "qk_mult": w.get("qk_mult", 1.0),
-                   "flops_per_step": fl, "kernel": kname, "parallelism": "single GPU"},
+                + (", Q and K multiplied by 4" if w.get("qk_mult", 1.0) != 1.0 else "")
+                + ("; dO N(0,1) rounded to bf16" if bwd else ""),
+        "config": config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
@@ -222,7 +288,9 @@ def main() -> int:
         "parity": parity,
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(x, causal, scale, min(args.cpu_heads, B * H))
+        heads = args.cpu_heads if args.cpu_heads is not None else (2 if bwd else 32)
+        res["cpu_baseline"] = cpu_baseline(x, causal, scale, min(heads, B * H), args.pass_,
+                                           do_bits)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -19,9 +19,9 @@ import math
 import os
 
 __all__ = [
-    "forward", "attn_fwd", "attn_fwd_f32", "kernel_name", "status_string",
-    "AttnError", "LibraryNotBuilt", "load_library", "LIB_PATH", "STATUS",
-    "flops",
+    "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "kernel_name",
+    "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
+    "LIB_PATH", "STATUS", "flops", "bwd_flops",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -38,8 +38,11 @@ EXPORTS = {
                  + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_fwd_f32": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4
                      + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_bwd": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4
+                 + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_kernel_name": (ctypes.c_char_p, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
+    "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
 }
 
 
@@ -82,6 +85,12 @@ def kernel_name(is_f32: bool, d: int, causal: bool):
     return None if n is None else n.decode()
 
 
+def bwd_kernel_name(d: int, causal: bool, which: int):
+    """Name of backward kernel ``which`` (0 row statistics, 1 dK/dV, 2 dQ)."""
+    n = load_library().attn_bwd_kernel_name(int(d), int(bool(causal)), int(which))
+    return None if n is None else n.decode()
+
+
 def attn_fwd(q, k, v, o, lse, B, H, T, d, causal, scale, stream=0) -> int:
     """Raw bf16 entry point: integer device addresses, returns the status."""
     return load_library().attn_fwd(q, k, v, o, lse, B, H, T, d, int(causal), float(scale),
@@ -94,11 +103,26 @@ def attn_fwd_f32(q, k, v, o, lse, B, H, T, d, causal, scale, stream=0) -> int:
                                        float(scale), stream or None)
 
 
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, T, d, causal, scale,
+             stream=0) -> int:
+    """Raw bf16 backward entry point: integer device addresses, returns the
+    status."""
+    return load_library().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, T, d,
+                                   int(causal), float(scale), stream or None)
+
+
 def flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
     """Counted FLOPs of one forward: the two T x T x d contractions,
     4*T*T*d per head, halved under a causal mask."""
     f = 4.0 * B * H * T * T * d
     return f / 2 if causal else f
+
+
+def bwd_flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
+    """Counted FLOPs of one backward: the five T x T x d contractions of the
+    gradient (S recomputed, dP, dV, dQ, dK), 2.5 times the forward's.  The
+    kernels recompute S and dP once more for dQ; that work is not counted."""
+    return 2.5 * flops(B, H, T, d, causal)
 
 
 def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
@@ -136,3 +160,48 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     if st != 0:
         raise AttnError(st, status_string(st))
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
+             dq=None, dk=None, dv=None, ws=None, stream=None):
+    """Gradients of the attention forward on bf16 torch tensors [B, H, T, d].
+
+    ``o`` and ``lse`` are what :func:`forward` returned for the same q, k, v,
+    causal and scale; ``dout`` is the gradient of o.  Returns (dq, dk, dv)
+    (bf16, q's shape).  ``ws`` is an optional float32 workspace of 2*B*H*T
+    elements (allocated when None); after the call it holds Delta and
+    lse*log2(e).
+    """
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o, dout must all have shape [B, H, T, d]")
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise ValueError("the backward takes bfloat16 q, k, v, o, dout")
+    for t in ts + (lse,):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous CUDA tensors")
+    B, H, T, d = q.shape
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, T] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if ws is None:
+        ws = torch.empty(2 * B * H * T, dtype=torch.float32, device=q.device)
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous bf16 tensors like q")
+    if ws.numel() < 2 * B * H * T or ws.dtype != torch.float32 or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous float32 tensor of 2*B*H*T elements")
+    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    with torch.cuda.device(q.device):
+        st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
+                      B, H, T, d, causal, scale, s)
+    if st != 0:
+        raise AttnError(st, status_string(st))
+    return dq, dk, dv

@@ -2,7 +2,8 @@
 
     python -m exact_attention_123_amd.build
 
-compiles ``csrc/attn_fwd.hip`` with hipcc into
+compiles ``csrc/attn_fwd.hip`` (forward) and ``csrc/attn_bwd.hip`` (backward)
+with hipcc into
 ``exact_attention_123_amd/libattn.so``.  The library exports the C ABI of
 ``include/attn.h``; the Python binding loads it with ctypes.
 """
@@ -15,7 +16,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 
@@ -45,7 +46,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, out: str = LIB) -> str:
     """Compile the library; returns its path.  Raises on compiler errors."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

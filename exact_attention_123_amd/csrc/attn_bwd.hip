@@ -1,0 +1,593 @@
+// Backward pass of exact scaled dot-product attention for AMD Instinct
+// MI355X (gfx950), behind the C ABI of include/attn.h.
+//
+// What is computed, per (batch, head), for the forward S = scale Q K^T
+// (causal mask optional), P = rowsoftmax(S), O = P V and an upstream
+// gradient dO of O:
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - Delta),  Delta_i = dO_i . O_i,
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// The pages state that this pass recomputes the scores the forward never
+// stored rather than reading them back ("Attention Mechanism: Computation &
+// Memory Patterns", section 4, "Computational Pattern"; its conclusion): P
+// is rebuilt tile by tile from Q, K and the forward's saved log-sum-exp,
+// P_ij = exp(S_ij - LSE_i), so no T x T matrix reaches device memory here
+// either.
+//
+// Three kernels, in stream order:
+//   1. prep : Delta_i = sum_c dO_ic O_ic and LSE_i * log2(e) per query row,
+//             into the caller's workspace.
+//   2. dkdv : one workgroup per 128 keys of a head (32 per wave), K and V of
+//             those keys held in registers; it walks 64-query tiles of Q and
+//             dO (staged in LDS) and accumulates dV^T += dO^T P and
+//             dK^T += Q^T dS in registers.
+//   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
+//             registers; it walks 64-key tiles of K and V (staged in LDS)
+//             and accumulates dQ^T += K^T dS^T.
+// dkdv and dq each recompute S and dP for their tiles; neither needs
+// atomics or a second pass, and every output element is written by exactly
+// one lane (the result does not depend on scheduling).
+//
+// All four contractions of a tile run on v_mfma_f32_32x32x16_bf16 (fp32
+// accumulate).  P and dS are rounded to bf16 (nearest-even) as MFMA
+// operands; S, P, dP, dS, Delta and the log-sum-exp stay fp32.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kWaves = 4;
+constexpr int kBK = 128;       // keys per dkdv workgroup
+constexpr int kBQ = 128;       // queries per dq workgroup
+constexpr int kTile = 64;      // rows of a staged Q/dO (dkdv) or K/V (dq) tile
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Raw buffer descriptor over `bytes` bytes at `base`: loads past the end
+// return zero without touching memory (ragged ends of the sequence).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// Row order of the A operand of a score-like MFMA (swap bits 2 and 3 of the
+// row index within 32).  With it, accumulator registers 8a .. 8a + 7 of lane
+// half h hold rows 16 a + 8 h + 0..7 of the tile: eight consecutive rows,
+// which is one B-operand slot of the MFMA that contracts over those rows.
+__device__ __forceinline__ int row_perm(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// LDS tile of rows of D bf16 (Q and dO in dkdv, K and V in dq): rows are
+// unpadded, and the 16-byte chunk c of row r sits at chunk c ^ swz(r).  The
+// tile is read two ways: row-wise, 16 bytes per lane (A operand of S and
+// dP; 16 lanes read 16 rows of one chunk), and column-wise with
+// ds_read_b64_tr_b16 (A operand of the dV/dK/dQ contractions; 32 lanes read
+// 4 rows x 4 chunks).  swz makes both conflict-free: it is one-to-one on
+// 16 consecutive rows, and on 4 aligned rows it moves the 4-chunk group by
+// the row within the four and the chunk within the group by the row's
+// 4-row block.  It depends only on r mod 16.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return 4 * (r & 3) + ((r >> 2) & 3);
+  else return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+template <int D>
+struct BwdTile {
+  static constexpr int RB = 2 * D;                   // bytes per row
+  static constexpr int NCH = D / 8;                  // 16-byte chunks per row
+  static constexpr int NDS = D / 16;                 // k-steps over d
+  static constexpr int NDT = D / 32;                 // 32-wide d tiles
+  static constexpr int TBYTES = kTile * RB;          // one staged tile
+  static constexpr int NBLK = TBYTES / 1024;         // 1 KiB direct-to-LDS blocks
+  static constexpr int PER = NBLK / kWaves;          // blocks per wave
+  static constexpr int RPK = 1024 / RB;              // rows per block
+  static_assert(PER * kWaves == NBLK, "tile split");
+};
+
+// Per-lane LDS addresses of the two read patterns (see swz).
+//  row read: lane (j, h) reads row row_perm(j) (+ 32 u), chunk 2 s + h.
+//  transposed read: ds_read_b64_tr_b16 hands lane i of a 16-lane group
+//  element (i % 4) of the 8 bytes read by lane 4 e + i / 4 of the group, in
+//  slot e.  Lane l of group g reads row 8 (g / 2) + l / 4 (+ 4 for the
+//  second read), bytes 8 (l % 2) of chunk 4 dt + 2 (g % 2) + (l / 2) % 2, so
+//  lane i of group g receives rows 8 (g / 2) + e (+ 4) of column
+//  32 dt + 16 (g % 2) + i: for the wave, lane (j, h) gets rows 8 h + 0..7
+//  of column 32 dt + j, the A operand [d][row] of a contraction over rows.
+template <int D>
+struct TileAddr {
+  using C = BwdTile<D>;
+  int row[C::NDS];
+  int tr[2][C::NDT];
+  __device__ __forceinline__ void init(int lane) {
+    const int j = lane & 31, h = lane >> 5;
+    const int r = row_perm(j);
+    const int f = swz<D>(r);
+#pragma unroll
+    for (int s = 0; s < C::NDS; ++s) row[s] = r * C::RB + 16 * ((2 * s + h) ^ f);
+    const int g = lane >> 4, l = lane & 15;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int rr = 8 * (g >> 1) + (l >> 2) + 4 * hi;
+      const int cc = 2 * (g & 1) + ((l >> 1) & 1);
+#pragma unroll
+      for (int dt = 0; dt < C::NDT; ++dt)
+        tr[hi][dt] = rr * C::RB + 16 * ((4 * dt + cc) ^ swz<D>(rr)) + 8 * (l & 1);
+    }
+  }
+};
+
+// 16 bytes at a byte address of an LDS tile.
+__device__ __forceinline__ bf16x8_t lds_row(const char* base, int off) {
+  return *reinterpret_cast<const bf16x8_t*>(base + off);
+}
+// A operand (8 consecutive rows of one column) by two transposing reads.
+__device__ __forceinline__ bf16x8_t lds_tr(const char* base, int off_lo, int off_hi) {
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + off_lo));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + off_hi));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Direct-to-LDS load of rows [row0, row0 + 64) of one head's [T][D] array
+// into a staged tile.  Wave w writes blocks PER w .. PER w + PER - 1; a block
+// is written by one instruction, lane L's 16 bytes landing at block offset
+// 16 L = (row RPK b + L / NCH, chunk L % NCH), so the lane loads the global
+// chunk that the swizzle puts there.  Rows >= T read as zero.
+template <int D>
+struct TileDma {
+  using C = BwdTile<D>;
+  int off[C::PER];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < C::PER; ++n) {
+      const int r = C::RPK * (C::PER * wave + n) + lane / C::NCH;
+      const int p = lane % C::NCH;
+      off[n] = r * C::RB + 16 * (p ^ swz<D>(r));
+    }
+  }
+  __device__ __forceinline__ void load(char* tile, const __bf16* head, int T, int row0,
+                                       int wave) const {
+    const int rem = max(T - row0, 0) * C::RB;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(head + (size_t)row0 * D, rem);
+#pragma unroll
+    for (int n = 0; n < C::PER; ++n) {
+      // (a plain local: passing an array element to the builtin directly
+      // makes the host-side instantiation drop the kernel)
+      const int o = off[n];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_void_t*)(tile + 1024 * (C::PER * wave + n)), 16, o, 0, 0, 0);
+    }
+  }
+};
+
+// Stores the 32 x D tile held as NDT transposed accumulators acc[dt]
+// (lane (j, h): row j, columns 32 dt + 8 g + 4 h + 0..3 in registers
+// 4 g .. 4 g + 3), times mul, as bf16 to out[row0 + j][.] if row0 + j < T.
+template <int D>
+__device__ __forceinline__ void store_rows(__bf16* out, const f32x16_t (&acc)[D / 32], float mul,
+                                           int row, int T, int h) {
+  if (row >= T) return;
+  __bf16* dst = out + (size_t)row * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __bf16 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = (__bf16)(acc[dt][4 * g + u] * mul);
+      u32x2_t bits;
+      std::memcpy(&bits, w, 8);
+      *reinterpret_cast<u32x2_t*>(dst + 32 * dt + 8 * g + 4 * h) = bits;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 1. prep: Delta_i = sum_c dO_ic O_ic (fp32) and LSE_i * log2(e), one row per
+// D / 8 lanes.  ws[0 .. n) = Delta, ws[n .. 2 n) = LSE * log2(e), n = B H T.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(
+    const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ ws, int64_t n) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.0f;
+  if (row < n) {
+    const bf16x8_t o = *reinterpret_cast<const bf16x8_t*>(O + row * D + 8 * sub);
+    const bf16x8_t g = *reinterpret_cast<const bf16x8_t*>(dO + row * D + 8 * sub);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < n && sub == 0) {
+    ws[row] = acc;
+    ws[n + row] = LSE[row] * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dkdv
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
+    __bf16* __restrict__ dV, int T, int BH, int nkb, float c, float scale) {
+  using C = BwdTile<D>;
+  constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
+
+  __shared__ __attribute__((aligned(1024))) char sQ[2][C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char sG[2][C::TBYTES];  // dO
+  __shared__ __attribute__((aligned(16))) float sL[2][kTile];       // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[2][kTile];       // Delta
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, h = lane >> 5;
+  // Heavy-first: under a causal mask the first key blocks see the most
+  // query tiles; consecutive ids walk the heads.
+  const int id = blockIdx.x;
+  const int kb = id / BH, bh = id % BH;
+  const size_t head = (size_t)bh * (size_t)T * D;
+  const int k0 = kb * kBK, kw0 = k0 + 32 * wave;
+  const int64_t n = (int64_t)BH * T;
+
+  // K and V of the wave's 32 keys: B operands [d][key] of S = Q K^T and
+  // dP = dO V^T; lane (j, h) holds row kw0 + j, d = 16 s + 8 h .. + 8.
+  bf16x8_t kf[NDS], vf[NDS];
+  {
+    const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + head, T * RB);
+    const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + head, T * RB);
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rK, (kw0 + j) * RB + (16 * s + 8 * h) * 2));
+      vf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rV, (kw0 + j) * RB + (16 * s + 8 * h) * 2));
+    }
+  }
+
+  TileAddr<D> ad;
+  ad.init(lane);
+  TileDma<D> dma;
+  dma.init(wave, lane);
+  const float* wsD = ws + (size_t)bh * T;
+  const float* wsL = ws + n + (size_t)bh * T;
+  // Row statistics of a query tile: one dword per lane of wave 0 (L) and
+  // wave 1 (Delta), lane L landing at 4 L; rows >= T read as zero.
+  auto stage = [&](int st, int qt) __attribute__((always_inline)) {
+    const int row0 = qt * kTile;
+    dma.load(sQ[st], Q + head, T, row0, wave);
+    dma.load(sG[st], dO + head, T, row0, wave);
+    if (wave < 2) {
+      const float* src = (wave == 0 ? wsL : wsD) + row0;
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(src, max(T - row0, 0) * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(wave == 0 ? sL[st] : sD[st]), 4,
+                                               lane * 4, 0, 0, 0);
+    }
+  };
+
+  f32x16_t dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk[dt] = f32x16_t{};
+    dv[dt] = f32x16_t{};
+  }
+
+  const int qt0 = CAUSAL ? k0 / kTile : 0;
+  const int nqt = (T + kTile - 1) / kTile;
+  if (qt0 < nqt) stage(0, qt0);
+  __syncthreads();
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int st = (qt - qt0) & 1;
+    if (qt + 1 < nqt) stage(st ^ 1, qt + 1);
+    const char* tq = sQ[st];
+    const char* tg = sG[st];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i0 = qt * kTile + 32 * u;
+      // every query of the sub-tile precedes every key of the wave
+      if (CAUSAL && i0 + 31 < kw0) continue;
+      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tq, 32 * u * RB + ad.row[s]), kf[s],
+                                                    S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tg, 32 * u * RB + ad.row[s]), vf[s],
+                                                     dP, 0, 0, 0);
+      }
+      // Register 8 a + e of lane (j, h) holds query i0 + 16 a + 8 h + e and
+      // key kw0 + j.
+      const bool edge = (CAUSAL && i0 < kw0 + 31) || kw0 + 31 >= T;
+      bf16x8_t pb[2], db[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int q8 = 32 * u + 16 * a + 8 * h;
+        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(&sL[st][q8]);
+        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&sL[st][q8 + 4]);
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&sD[st][q8]);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&sD[st][q8 + 4]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lse2 = e < 4 ? l0[e] : l1[e - 4];
+          const float dl = e < 4 ? d0[e] : d1[e - 4];
+          float p = exp2_hw(fmaf(S[8 * a + e], c, -lse2));
+          if (edge) {
+            const int key = kw0 + j, query = i0 + 16 * a + 8 * h + e;
+            if (key >= T || (CAUSAL && key > query)) p = 0.0f;
+          }
+          pb[a][e] = (__bf16)p;
+          db[a][e] = (__bf16)(p * (dP[8 * a + e] - dl));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 queries.
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int ro = (32 * u + 16 * a) * RB;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_tr(tg, ro + ad.tr[0][dt], ro + ad.tr[1][dt]), pb[a], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_tr(tq, ro + ad.tr[0][dt], ro + ad.tr[1][dt]), db[a], dk[dt], 0, 0, 0);
+        }
+      }
+    }
+    // waits for the next stage's loads too (they have landed in LDS when
+    // the load counter drops) and frees this stage
+    __syncthreads();
+  }
+
+  store_rows<D>(dK + head, dk, scale, kw0 + j, T, h);
+  store_rows<D>(dV + head, dv, 1.0f, kw0 + j, T, h);
+}
+
+// ---------------------------------------------------------------------------
+// 3. dq
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int T,
+    int BH, int nqb, float c, float scale) {
+  using C = BwdTile<D>;
+  constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
+
+  __shared__ __attribute__((aligned(1024))) char sK[2][C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV[2][C::TBYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 31, h = lane >> 5;
+  // Heavy-first: the last query blocks see the most key tiles.
+  const int id = blockIdx.x;
+  const int qb = nqb - 1 - id / BH, bh = id % BH;
+  const size_t head = (size_t)bh * (size_t)T * D;
+  const int q0 = qb * kBQ, qw0 = q0 + 32 * wave, qg = qw0 + j;
+  const int64_t n = (int64_t)BH * T;
+
+  // Q and dO of the wave's 32 queries: B operands [d][query] of S^T = K Q^T
+  // and dP^T = V dO^T.
+  bf16x8_t qf[NDS], gf[NDS];
+  {
+    const __amdgpu_buffer_rsrc_t rQ = make_rsrc(Q + head, T * RB);
+    const __amdgpu_buffer_rsrc_t rG = make_rsrc(dO + head, T * RB);
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rQ, qg * RB + (16 * s + 8 * h) * 2));
+      gf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rG, qg * RB + (16 * s + 8 * h) * 2));
+    }
+  }
+  const float dl = qg < T ? ws[(size_t)bh * T + qg] : 0.0f;
+  const float lse2 = qg < T ? ws[n + (size_t)bh * T + qg] : 0.0f;
+
+  TileAddr<D> ad;
+  ad.init(lane);
+  TileDma<D> dma;
+  dma.init(wave, lane);
+  auto stage = [&](int st, int t) __attribute__((always_inline)) {
+    dma.load(sK[st], K + head, T, t * kTile, wave);
+    dma.load(sV[st], V + head, T, t * kTile, wave);
+  };
+
+  f32x16_t dq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dq[dt] = f32x16_t{};
+
+  const int kv_end = CAUSAL ? min(T, q0 + kBQ) : T;
+  const int nkt = (kv_end + kTile - 1) / kTile;
+  if (nkt > 0) stage(0, 0);
+  __syncthreads();
+
+  for (int t = 0; t < nkt; ++t) {
+    const int st = t & 1;
+    if (t + 1 < nkt) stage(st ^ 1, t + 1);
+    const char* tk = sK[st];
+    const char* tv = sV[st];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kv0 = t * kTile + 32 * u;
+      // every key of the sub-tile follows every query of the wave
+      if (CAUSAL && kv0 > qw0 + 31) continue;
+      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tk, 32 * u * RB + ad.row[s]), qf[s],
+                                                    S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tv, 32 * u * RB + ad.row[s]), gf[s],
+                                                     dP, 0, 0, 0);
+      }
+      // Register 8 a + e of lane (j, h) holds key kv0 + 16 a + 8 h + e and
+      // query qg.
+      const bool edge = (CAUSAL && kv0 + 31 > qw0) || kv0 + 31 >= T;
+      bf16x8_t db[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float p = exp2_hw(fmaf(S[8 * a + e], c, -lse2));
+          if (edge) {
+            const int key = kv0 + 16 * a + 8 * h + e;
+            if (key >= T || (CAUSAL && key > qg)) p = 0.0f;
+          }
+          db[a][e] = (__bf16)(p * (dP[8 * a + e] - dl));
+        }
+      // dQ^T += K^T dS^T over the sub-tile's 32 keys.
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int ro = (32 * u + 16 * a) * RB;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_tr(tk, ro + ad.tr[0][dt], ro + ad.tr[1][dt]), db[a], dq[dt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  store_rows<D>(dQ + head, dq, scale, qg, T, h);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - 1;
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+attn_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+template <int D>
+const void* dkdv_kernel(int causal) {
+  return causal ? (const void*)attn_bwd_dkdv_kernel<D, true>
+                : (const void*)attn_bwd_dkdv_kernel<D, false>;
+}
+template <int D>
+const void* dq_kernel(int causal) {
+  return causal ? (const void*)attn_bwd_dq_kernel<D, true>
+                : (const void*)attn_bwd_dq_kernel<D, false>;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, float* ws,
+                     int64_t B, int64_t H, int64_t T, int64_t d, int causal, float scale,
+                     hipStream_t stream) {
+  if (B < 0 || H < 0 || T < 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || H == 0 || T == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
+  if ((T + 256) * d * 2 > kMaxHeadBytes) return ATTN_ERR_SHAPE;
+  if (B > (int64_t(1) << 31) / H) return ATTN_ERR_SHAPE;
+  const int64_t BH = B * H;
+  const int64_t nblk = (T + 127) / 128;
+  if (BH > INT32_MAX / nblk) return ATTN_ERR_SHAPE;
+  if (BH > (INT64_MAX / 8) / (T * d * 2)) return ATTN_ERR_SHAPE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return ATTN_ERR_ALIGN;
+  if (((uintptr_t)lse | (uintptr_t)ws) & 3u) return ATTN_ERR_ALIGN;
+  const int64_t nb = BH * T * d * 2, lb = BH * T * 4, wb = 2 * lb;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const int64_t in_bytes[6] = {nb, nb, nb, nb, nb, lb};
+  void* outs[4] = {dq, dk, dv, ws};
+  const int64_t out_bytes[4] = {nb, nb, nb, wb};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return ATTN_ERR_ARG;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return ATTN_ERR_ARG;
+  }
+  attn_status st = check_device();
+  if (st != ATTN_OK) return st;
+
+  const int t = (int)T, bh = (int)BH;
+  const int64_t n = BH * T;
+  const float c = scale * kLog2e;
+  {
+    const int rows_per_block = kThreads / (int)(d / 8);
+    const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block));
+    const __bf16* ob = (const __bf16*)o;
+    const __bf16* gb = (const __bf16*)dout;
+    void* args[] = {(void*)&ob, (void*)&gb, (void*)&lse, (void*)&ws, (void*)&n};
+    const void* kern = d == 64 ? (const void*)attn_bwd_prep_kernel<64>
+                               : (const void*)attn_bwd_prep_kernel<128>;
+    if (hipLaunchKernel(kern, grid, dim3(kThreads), args, 0, stream) != hipSuccess)
+      return ATTN_ERR_LAUNCH;
+  }
+  const __bf16 *qb = (const __bf16*)q, *kb = (const __bf16*)k, *vb = (const __bf16*)v,
+               *gb = (const __bf16*)dout;
+  const float* wsc = ws;
+  {
+    int nkb = (int)((T + kBK - 1) / kBK);
+    __bf16 *dkb = (__bf16*)dk, *dvb = (__bf16*)dv;
+    void* args[] = {(void*)&qb, (void*)&kb,  (void*)&vb, (void*)&gb,  (void*)&wsc, (void*)&dkb,
+                    (void*)&dvb, (void*)&t,  (void*)&bh, (void*)&nkb, (void*)&c,   (void*)&scale};
+    const void* kern = d == 64 ? dkdv_kernel<64>(causal) : dkdv_kernel<128>(causal);
+    if (hipLaunchKernel(kern, dim3((unsigned)(bh * nkb)), dim3(kThreads), args, 0, stream) !=
+        hipSuccess)
+      return ATTN_ERR_LAUNCH;
+  }
+  {
+    int nqb = (int)((T + kBQ - 1) / kBQ);
+    __bf16* dqb = (__bf16*)dq;
+    void* args[] = {(void*)&qb, (void*)&kb, (void*)&vb,  (void*)&gb, (void*)&wsc, (void*)&dqb,
+                    (void*)&t,  (void*)&bh, (void*)&nqb, (void*)&c,  (void*)&scale};
+    const void* kern = d == 64 ? dq_kernel<64>(causal) : dq_kernel<128>(causal);
+    if (hipLaunchKernel(kern, dim3((unsigned)(bh * nqb)), dim3(kThreads), args, 0, stream) !=
+        hipSuccess)
+      return ATTN_ERR_LAUNCH;
+  }
+  return ATTN_OK;
+}
+
+const char* attn_bwd_kernel_name(int64_t d, int causal, int which) {
+  if ((d != 64 && d != 128) || (causal != 0 && causal != 1) || which < 0 || which > 2)
+    return nullptr;
+  static const char* names[2][2][3] = {
+      {{"attn_bwd_prep_d64", "attn_bwd_dkdv_bf16_d64_full_bk128_bq64_w4",
+        "attn_bwd_dq_bf16_d64_full_bq128_bk64_w4"},
+       {"attn_bwd_prep_d64", "attn_bwd_dkdv_bf16_d64_causal_bk128_bq64_w4",
+        "attn_bwd_dq_bf16_d64_causal_bq128_bk64_w4"}},
+      {{"attn_bwd_prep_d128", "attn_bwd_dkdv_bf16_d128_full_bk128_bq64_w4",
+        "attn_bwd_dq_bf16_d128_full_bq128_bk64_w4"},
+       {"attn_bwd_prep_d128", "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4",
+        "attn_bwd_dq_bf16_d128_causal_bq128_bk64_w4"}}};
+  return names[d == 128 ? 1 : 0][causal][which];
+}
+
+}  // extern "C"

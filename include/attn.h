@@ -91,6 +91,46 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v,
                          int64_t T, int64_t d, int causal, float scale,
                          hipStream_t stream);
 
+/*
+ * bfloat16 backward pass ("Attention Mechanism: Computation & Memory
+ * Patterns", section 4 and its conclusion: the pass recomputes the scores
+ * the forward did not store).  For the forward above and an upstream
+ * gradient dO of O it computes, per (batch, head),
+ *
+ *   dV = P^T dO
+ *   dS_ij = P_ij (dP_ij - Delta_i),  dP = dO V^T,  Delta_i = sum_c dO_ic O_ic
+ *   dQ = scale dS K,   dK = scale dS^T Q
+ *
+ * with P_ij = exp(S_ij - LSE_i) rebuilt tile by tile from q, k and the
+ * forward's lse (masked entries are 0, so the causal mask passes no
+ * gradient).  No T x T matrix is stored.
+ *   q, k, v, o, dout: const __hip_bfloat16 [B][H][T][d] (o and lse as the
+ *          forward wrote them for the same q, k, v, causal and scale);
+ *   lse:   const float [B][H][T];
+ *   dq, dk, dv: __hip_bfloat16 [B][H][T][d], written (nearest-even);
+ *   ws:    float workspace of 2*B*H*T elements, owned by the caller.  On
+ *          return ws[0 .. B*H*T) holds Delta and ws[B*H*T .. 2*B*H*T) holds
+ *          lse * log2(e), both [B][H][T].
+ *   B, H, T, d, causal, scale: as for attn_fwd.
+ * S, P, dP, dS, Delta are fp32; P and dS are rounded to bf16 (nearest-even)
+ * as inputs of the bf16 MFMA contractions, which accumulate in fp32.  Three
+ * kernels are enqueued on `stream` in order (row statistics, dK/dV, dQ);
+ * every output element is written exactly once, so results do not depend on
+ * scheduling.  Pointers: 16-byte aligned (lse, ws: 4-byte).  dq, dk, dv and
+ * ws must not overlap each other or any input.  Errors as for attn_fwd.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk,
+                     void* dv, float* ws, int64_t B, int64_t H, int64_t T,
+                     int64_t d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Name of kernel `which` (0 = row statistics, 1 = dK/dV, 2 = dQ) that
+ * attn_bwd launches for head dimension d and the causal flag, e.g.
+ * "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4".  NULL if unsupported.
+ */
+const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
+
 /* Static description of a status code (never NULL). */
 const char* attn_status_string(attn_status s);
 

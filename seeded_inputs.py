@@ -26,6 +26,7 @@ __all__ = [
     "WORKLOADS",
     "sample_rows",
     "make_workload",
+    "make_dout",
 ]
 
 
@@ -121,6 +122,14 @@ def make_qkv(B: int, H: int, T: int, d: int, *, dtype: str = "bf16",
         arrs.append(f32_to_bf16_bits(a) if dtype == "bf16" else a)
     return QKV(dtype=dtype, q=arrs[0], k=arrs[1], v=arrs[2], seed=seed,
                qk_mult=qk_mult)
+
+
+def make_dout(B: int, H: int, T: int, d: int, *, seed: int) -> np.ndarray:
+    """Upstream gradient dO of the output for the backward pass: i.i.d.
+    standard normal (float32) from PCG64(seed), rounded to bfloat16; returns
+    the uint16 bit patterns, [B, H, T, d]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return f32_to_bf16_bits(rng.standard_normal((B, H, T, d), dtype=np.float32))
 
 
 def sample_rows(T: int, n: int, seed: int, heads: int) -> np.ndarray:

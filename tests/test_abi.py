@@ -115,3 +115,42 @@ def test_flops_convention():
     assert ea.flops(1, 32, 8192, 128, True) == pytest.approx(549.755813888e9)
     assert ea.flops(4, 16, 4096, 128, False) == pytest.approx(549.755813888e9)
     assert ea.flops(1, 1, 256, 64, True) == 2 * 256 * 256 * 64
+
+
+def call_bwd(q=A, k=2 * A, v=3 * A, o=4 * A, do=5 * A, lse=6 * A, dq=7 * A, dk=8 * A,
+             dv=9 * A, ws=10 * A, B=1, H=1, T=8, d=64, causal=1, scale=0.125):
+    return ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, T, d, causal, scale)
+
+
+@no_gpu_only
+def test_bwd_validation_errors():
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert call_bwd(**{name: 0}) == 1, name
+    assert call_bwd(B=-1) == 2
+    assert call_bwd(T=(1 << 31) // 256, d=128) == 2
+    for d in (0, 32, 96, 256):
+        assert call_bwd(d=d) == 3
+    for s in (math.nan, math.inf):
+        assert call_bwd(scale=s) == 4
+    assert call_bwd(dq=7 * A + 8) == 5
+    assert call_bwd(do=5 * A + 4) == 5
+    assert call_bwd(ws=10 * A + 2) == 5
+    assert call_bwd(causal=3) == 6
+    assert call_bwd(dq=A) == 6           # dq aliases q
+    assert call_bwd(dk=9 * A) == 6       # dk aliases dv
+    assert call_bwd(ws=6 * A) == 6       # ws overlaps lse
+
+
+def test_bwd_empty_problem_is_a_no_op():
+    for kw in (dict(B=0), dict(H=0), dict(T=0)):
+        assert call_bwd(q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, ws=0, **kw) == 0
+
+
+def test_bwd_kernel_names_and_flops():
+    assert ea.bwd_kernel_name(128, True, 1).startswith("attn_bwd_dkdv_bf16_d128_causal")
+    assert ea.bwd_kernel_name(64, False, 2).startswith("attn_bwd_dq_bf16_d64_full")
+    assert ea.bwd_kernel_name(128, True, 0) == "attn_bwd_prep_d128"
+    assert ea.bwd_kernel_name(96, True, 1) is None
+    assert ea.bwd_kernel_name(128, True, 3) is None
+    # five T x T x d contractions: 2.5 times the forward
+    assert ea.bwd_flops(1, 32, 8192, 128, True) == pytest.approx(2.5 * 549.755813888e9)
