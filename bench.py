@@ -77,13 +77,14 @@ def cpu_baseline(x, causal: bool, scale: float, heads: int, pass_: str, do_bits=
     from seeded_inputs import bf16_bits_to_f32
 
     B, H, T, d = x.shape
+    G = H // x.k.shape[1]  # query heads per key/value head
     t0 = time.perf_counter()
     done = 0
     for i in range(heads):
         b, h = divmod(i, H)
         if pass_ == "fwd":
-            oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h), causal=causal,
-                                  scale=scale)
+            oracle.attention_head(x.q64(b, h), x.k64(b, h // G), x.v64(b, h // G),
+                                  causal=causal, scale=scale)
         else:
             g = bf16_bits_to_f32(do_bits[b, h]).astype("float64")
             oracle.attention_head_bwd(x.q64(b, h), x.k64(b, h), x.v64(b, h), g,
@@ -138,8 +139,10 @@ def main() -> int:
     causal = w["causal"][0]
     B, H, T, d, dt = w["B"], w["H"], w["T"], w["d"], w["dtype"]
     bwd = args.pass_ == "bwd"
-    if bwd and dt != "bf16":
-        print("the backward pass is bf16 only", file=sys.stderr)
+    Hkv = w.get("H_kv", H)
+    if bwd and (dt != "bf16" or Hkv != H):
+        print("bench --pass bwd takes bf16 workloads without grouped key/value heads",
+              file=sys.stderr)
         return 2
     scale = 1.0 / math.sqrt(d)
     dev = torch.device("cuda:0")
@@ -195,8 +198,9 @@ def main() -> int:
         if not bwd:
             O, L = to64(out), lse.cpu().numpy()
             eo = el = 0.0
+            G = H // Hkv
             for (b, h) in heads:
-                ref = oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h),
+                ref = oracle.attention_head(x.q64(b, h), x.k64(b, h // G), x.v64(b, h // G),
                                             causal=causal, scale=scale, rows=rows)
                 eo = max(eo, float(np.abs(O[b, h][rows] - ref["O"]).max()))
                 el = max(el, float(np.abs(L[b, h][rows] - ref["LSE"]).max()))
@@ -256,7 +260,8 @@ def main() -> int:
     peak = PEAK_TFLOPS[dt]
     traffic = measured_traffic(kname, args.workload, args.pass_)
 
-    config = {"workload": args.workload, "pass": args.pass_, "B": B, "H": H, "T": T, "d": d,
+    config = {"workload": args.workload, "pass": args.pass_, "B": B, "H": H, "H_kv": Hkv,
+              "T": T, "d": d,
               "causal": causal, "scale": scale, "qk_mult": w.get("qk_mult", 1.0),
               "flops_per_step": fl, "kernel": kname, "parallelism": "single GPU"}
     if bwd:

@@ -19,7 +19,8 @@ import math
 import os
 
 __all__ = [
-    "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "kernel_name",
+    "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_fwd_gqa",
+    "attn_bwd_gqa", "kernel_name",
     "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
     "LIB_PATH", "STATUS", "flops", "bwd_flops",
 ]
@@ -40,6 +41,10 @@ EXPORTS = {
                      + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_bwd": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4
                  + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_fwd_gqa": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5
+                     + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_bwd_gqa": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5
+                     + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_kernel_name": (ctypes.c_char_p, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
@@ -103,6 +108,19 @@ def attn_fwd_f32(q, k, v, o, lse, B, H, T, d, causal, scale, stream=0) -> int:
                                        float(scale), stream or None)
 
 
+def attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, T, d, causal, scale, stream=0) -> int:
+    """Raw grouped-query bf16 forward: integer device addresses."""
+    return load_library().attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, T, d, int(causal),
+                                       float(scale), stream or None)
+
+
+def attn_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, H_kv, T, d, causal, scale,
+                 stream=0) -> int:
+    """Raw grouped-query bf16 backward: integer device addresses."""
+    return load_library().attn_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, H_kv, T, d,
+                                       int(causal), float(scale), stream or None)
+
+
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, T, d, causal, scale,
              stream=0) -> int:
     """Raw bf16 backward entry point: integer device addresses, returns the
@@ -127,21 +145,28 @@ def bwd_flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
 
 def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None,
             stream=None):
-    """Fused attention forward on torch tensors [B, H, T, d] (bf16 or fp32).
+    """Fused attention forward on torch tensors (bf16 or fp32).
 
-    Returns (o, lse): o has q's dtype and shape; lse is float32 [B, H, T].
-    Runs on ``stream`` (a torch.cuda.Stream) or the current stream.
+    q: [B, H, T, d]; k, v: [B, H_kv, T, d] with H_kv dividing H (grouped
+    query heads, bf16 only, when H_kv < H).  Returns (o, lse): o has q's
+    dtype and shape; lse is float32 [B, H, T].  Runs on ``stream`` (a
+    torch.cuda.Stream) or the current stream.
     """
     import torch
 
-    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
-        raise ValueError("q, k, v must all have shape [B, H, T, d]")
+    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4:
+        raise ValueError("q must be [B, H, T, d] and k, v [B, H_kv, T, d]")
+    B, H, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2:] != q.shape[2:] or Hkv < 1 or H % Hkv:
+        raise ValueError("k, v must be [B, H_kv, T, d] with H_kv dividing H")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if q.dtype == torch.float32 and Hkv != H:
+        raise ValueError("grouped key/value heads are supported in bfloat16 only")
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous CUDA tensors")
-    B, H, T, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -153,10 +178,13 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    fn = attn_fwd_f32 if q.dtype == torch.float32 else attn_fwd
     with torch.cuda.device(q.device):
-        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                B, H, T, d, causal, scale, s)
+        if q.dtype == torch.float32:
+            st = attn_fwd_f32(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, T, d, causal, scale, s)
+        else:
+            st = attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, Hkv, T, d, causal, scale, s)
     if st != 0:
         raise AttnError(st, status_string(st))
     return out, lse
@@ -164,44 +192,48 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
 
 def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
              dq=None, dk=None, dv=None, ws=None, stream=None):
-    """Gradients of the attention forward on bf16 torch tensors [B, H, T, d].
+    """Gradients of the attention forward on bf16 torch tensors.
 
-    ``o`` and ``lse`` are what :func:`forward` returned for the same q, k, v,
+    q, o, dout: [B, H, T, d]; k, v: [B, H_kv, T, d] (H_kv dividing H).  ``o``
+    and ``lse`` are what :func:`forward` returned for the same q, k, v,
     causal and scale; ``dout`` is the gradient of o.  Returns (dq, dk, dv)
-    (bf16, q's shape).  ``ws`` is an optional float32 workspace of 2*B*H*T
+    shaped like q, k, v.  ``ws`` is an optional float32 workspace of 2*B*H*T
     elements (allocated when None); after the call it holds Delta and
     lse*log2(e).
     """
     import torch
 
+    if q.dim() != 4 or o.shape != q.shape or dout.shape != q.shape or k.shape != v.shape:
+        raise ValueError("q, o, dout must be [B, H, T, d] and k, v [B, H_kv, T, d]")
+    B, H, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.dim() != 4 or k.shape[0] != B or k.shape[2:] != q.shape[2:] or Hkv < 1 or H % Hkv:
+        raise ValueError("k, v must be [B, H_kv, T, d] with H_kv dividing H")
     ts = (q, k, v, o, dout)
-    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
-        raise ValueError("q, k, v, o, dout must all have shape [B, H, T, d]")
     if any(t.dtype != torch.bfloat16 for t in ts):
         raise ValueError("the backward takes bfloat16 q, k, v, o, dout")
     for t in ts + (lse,):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("all tensors must be contiguous CUDA tensors")
-    B, H, T, d = q.shape
     if lse.shape != (B, H, T) or lse.dtype != torch.float32:
         raise ValueError("lse must be a float32 [B, H, T] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
     if ws is None:
         ws = torch.empty(2 * B * H * T, dtype=torch.float32, device=q.device)
-    for t in (dq, dk, dv):
-        if t.shape != q.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous bf16 tensors like q")
+    for t, like in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != like.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous bf16 tensors like q, k, v")
     if ws.numel() < 2 * B * H * T or ws.dtype != torch.float32 or not ws.is_contiguous():
         raise ValueError("ws must be a contiguous float32 tensor of 2*B*H*T elements")
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     with torch.cuda.device(q.device):
-        st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws.data_ptr(),
-                      B, H, T, d, causal, scale, s)
+        st = attn_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), ws.data_ptr(), B, H, Hkv, T, d, causal, scale, s)
     if st != 0:
         raise AttnError(st, status_string(st))
     return dq, dk, dv

@@ -233,7 +233,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
-    __bf16* __restrict__ dV, int T, int BH, int nkb, float c, float scale) {
+    __bf16* __restrict__ dV, int T, int BHkv, int G, int nkb, float c, float scale) {
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
 
@@ -246,12 +246,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, h = lane >> 5;
   // Heavy-first: under a causal mask the first key blocks see the most
-  // query tiles; consecutive ids walk the heads.
+  // query tiles; consecutive ids walk the key/value heads.
   const int id = blockIdx.x;
-  const int kb = id / BH, bh = id % BH;
-  const size_t head = (size_t)bh * (size_t)T * D;
+  const int kb = id / BHkv, bhkv = id % BHkv;
+  const size_t head = (size_t)bhkv * (size_t)T * D;
   const int k0 = kb * kBK, kw0 = k0 + 32 * wave;
-  const int64_t n = (int64_t)BH * T;
+  const int64_t n = (int64_t)BHkv * G * T;
 
   // K and V of the wave's 32 keys: B operands [d][key] of S = Q K^T and
   // dP = dO V^T; lane (j, h) holds row kw0 + j, d = 16 s + 8 h .. + 8.
@@ -270,16 +270,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   ad.init(lane);
   TileDma<D> dma;
   dma.init(wave, lane);
-  const float* wsD = ws + (size_t)bh * T;
-  const float* wsL = ws + n + (size_t)bh * T;
-  // Row statistics of a query tile: one dword per lane of wave 0 (L) and
-  // wave 1 (Delta), lane L landing at 4 L; rows >= T read as zero.
-  auto stage = [&](int st, int qt) __attribute__((always_inline)) {
+  // Query tile `qt` of member `m` of the group (query head bhkv G + m).
+  // Row statistics: one dword per lane of wave 0 (L) and wave 1 (Delta),
+  // lane L landing at 4 L; rows >= T read as zero.
+  auto stage = [&](int st, int m, int qt) __attribute__((always_inline)) {
+    const size_t bhq = (size_t)bhkv * G + m;
+    const size_t qhead = bhq * (size_t)T * D;
     const int row0 = qt * kTile;
-    dma.load(sQ[st], Q + head, T, row0, wave);
-    dma.load(sG[st], dO + head, T, row0, wave);
+    dma.load(sQ[st], Q + qhead, T, row0, wave);
+    dma.load(sG[st], dO + qhead, T, row0, wave);
     if (wave < 2) {
-      const float* src = (wave == 0 ? wsL : wsD) + row0;
+      const float* src = ws + (wave == 0 ? n : 0) + bhq * T + row0;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(src, max(T - row0, 0) * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(wave == 0 ? sL[st] : sD[st]), 4,
                                                lane * 4, 0, 0, 0);
@@ -293,14 +294,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     dv[dt] = f32x16_t{};
   }
 
+  // The walk: for each of the G query heads of the group, the query tiles
+  // from the block's first visible one to the end.
   const int qt0 = CAUSAL ? k0 / kTile : 0;
   const int nqt = (T + kTile - 1) / kTile;
-  if (qt0 < nqt) stage(0, qt0);
+  const int per = nqt - qt0;  // > 0: k0 < T
+  const int nit = G * per;
+  stage(0, 0, qt0);
   __syncthreads();
 
-  for (int qt = qt0; qt < nqt; ++qt) {
-    const int st = (qt - qt0) & 1;
-    if (qt + 1 < nqt) stage(st ^ 1, qt + 1);
+  for (int it = 0; it < nit; ++it) {
+    const int st = it & 1;
+    if (it + 1 < nit) stage(st ^ 1, (it + 1) / per, qt0 + (it + 1) % per);
+    const int qt = qt0 + it % per;
     const char* tq = sQ[st];
     const char* tg = sG[st];
 #pragma unroll
@@ -369,7 +375,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int T,
-    int BH, int nqb, float c, float scale) {
+    int BH, int nqb, int G, float c, float scale) {
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
 
@@ -379,10 +385,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, h = lane >> 5;
-  // Heavy-first: the last query blocks see the most key tiles.
+  // Heavy-first: the last query blocks see the most key tiles.  Head slot
+  // hid is member hid / NKV of key/value group hid % NKV, so that the query
+  // heads of one group share an XCD (as in the forward).
   const int id = blockIdx.x;
-  const int qb = nqb - 1 - id / BH, bh = id % BH;
+  const int qb = nqb - 1 - id / BH, hid = id % BH;
+  const int nkv = BH / G, bhkv = hid % nkv, bh = bhkv * G + hid / nkv;
   const size_t head = (size_t)bh * (size_t)T * D;
+  const size_t kvhead = (size_t)bhkv * (size_t)T * D;
   const int q0 = qb * kBQ, qw0 = q0 + 32 * wave, qg = qw0 + j;
   const int64_t n = (int64_t)BH * T;
 
@@ -406,8 +416,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   TileDma<D> dma;
   dma.init(wave, lane);
   auto stage = [&](int st, int t) __attribute__((always_inline)) {
-    dma.load(sK[st], K + head, T, t * kTile, wave);
-    dma.load(sV[st], V + head, T, t * kTile, wave);
+    dma.load(sK[st], K + kvhead, T, t * kTile, wave);
+    dma.load(sV[st], V + kvhead, T, t * kTile, wave);
   };
 
   f32x16_t dq[NDT];
@@ -501,19 +511,20 @@ const void* dq_kernel(int causal) {
 
 extern "C" {
 
-attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                     const void* dout, const float* lse, void* dq, void* dk, void* dv, float* ws,
-                     int64_t B, int64_t H, int64_t T, int64_t d, int causal, float scale,
-                     hipStream_t stream) {
-  if (B < 0 || H < 0 || T < 0) return ATTN_ERR_SHAPE;
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* ws, int64_t B, int64_t H, int64_t H_kv, int64_t T, int64_t d,
+                         int causal, float scale, hipStream_t stream) {
+  if (B < 0 || H < 0 || T < 0 || H_kv < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  if ((H_kv == 0) != (H == 0) || (H_kv > 0 && H % H_kv != 0)) return ATTN_ERR_SHAPE;
   if (B == 0 || H == 0 || T == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !ws) return ATTN_ERR_NULL;
   if ((T + 256) * d * 2 > kMaxHeadBytes) return ATTN_ERR_SHAPE;
   if (B > (int64_t(1) << 31) / H) return ATTN_ERR_SHAPE;
-  const int64_t BH = B * H;
+  const int64_t BH = B * H, BHkv = B * H_kv;
   const int64_t nblk = (T + 127) / 128;
   if (BH > INT32_MAX / nblk) return ATTN_ERR_SHAPE;
   if (BH > (INT64_MAX / 8) / (T * d * 2)) return ATTN_ERR_SHAPE;
@@ -521,11 +532,11 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
     return ATTN_ERR_ALIGN;
   if (((uintptr_t)lse | (uintptr_t)ws) & 3u) return ATTN_ERR_ALIGN;
-  const int64_t nb = BH * T * d * 2, lb = BH * T * 4, wb = 2 * lb;
+  const int64_t nb = BH * T * d * 2, kb = BHkv * T * d * 2, lb = BH * T * 4, wb = 2 * lb;
   const void* ins[6] = {q, k, v, o, dout, lse};
-  const int64_t in_bytes[6] = {nb, nb, nb, nb, nb, lb};
+  const int64_t in_bytes[6] = {nb, kb, kb, nb, nb, lb};
   void* outs[4] = {dq, dk, dv, ws};
-  const int64_t out_bytes[4] = {nb, nb, nb, wb};
+  const int64_t out_bytes[4] = {nb, kb, kb, wb};
   for (int a = 0; a < 4; ++a) {
     for (int b = 0; b < 6; ++b)
       if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return ATTN_ERR_ARG;
@@ -535,7 +546,7 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   attn_status st = check_device();
   if (st != ATTN_OK) return st;
 
-  const int t = (int)T, bh = (int)BH;
+  const int t = (int)T, bh = (int)BH, bhkv = (int)BHkv, g = (int)(H / H_kv);
   const int64_t n = BH * T;
   const float c = scale * kLog2e;
   {
@@ -549,30 +560,40 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
     if (hipLaunchKernel(kern, grid, dim3(kThreads), args, 0, stream) != hipSuccess)
       return ATTN_ERR_LAUNCH;
   }
-  const __bf16 *qb = (const __bf16*)q, *kb = (const __bf16*)k, *vb = (const __bf16*)v,
+  const __bf16 *qb = (const __bf16*)q, *kb_ = (const __bf16*)k, *vb = (const __bf16*)v,
                *gb = (const __bf16*)dout;
   const float* wsc = ws;
   {
     int nkb = (int)((T + kBK - 1) / kBK);
     __bf16 *dkb = (__bf16*)dk, *dvb = (__bf16*)dv;
-    void* args[] = {(void*)&qb, (void*)&kb,  (void*)&vb, (void*)&gb,  (void*)&wsc, (void*)&dkb,
-                    (void*)&dvb, (void*)&t,  (void*)&bh, (void*)&nkb, (void*)&c,   (void*)&scale};
+    void* args[] = {(void*)&qb,  (void*)&kb_, (void*)&vb, (void*)&gb,  (void*)&wsc,
+                    (void*)&dkb, (void*)&dvb, (void*)&t,  (void*)&bhkv, (void*)&g,
+                    (void*)&nkb, (void*)&c,   (void*)&scale};
     const void* kern = d == 64 ? dkdv_kernel<64>(causal) : dkdv_kernel<128>(causal);
-    if (hipLaunchKernel(kern, dim3((unsigned)(bh * nkb)), dim3(kThreads), args, 0, stream) !=
+    if (hipLaunchKernel(kern, dim3((unsigned)(bhkv * nkb)), dim3(kThreads), args, 0, stream) !=
         hipSuccess)
       return ATTN_ERR_LAUNCH;
   }
   {
     int nqb = (int)((T + kBQ - 1) / kBQ);
     __bf16* dqb = (__bf16*)dq;
-    void* args[] = {(void*)&qb, (void*)&kb, (void*)&vb,  (void*)&gb, (void*)&wsc, (void*)&dqb,
-                    (void*)&t,  (void*)&bh, (void*)&nqb, (void*)&c,  (void*)&scale};
+    void* args[] = {(void*)&qb, (void*)&kb_, (void*)&vb,  (void*)&gb, (void*)&wsc,
+                    (void*)&dqb, (void*)&t,  (void*)&bh,  (void*)&nqb, (void*)&g,
+                    (void*)&c,  (void*)&scale};
     const void* kern = d == 64 ? dq_kernel<64>(causal) : dq_kernel<128>(causal);
     if (hipLaunchKernel(kern, dim3((unsigned)(bh * nqb)), dim3(kThreads), args, 0, stream) !=
         hipSuccess)
       return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
+}
+
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, float* ws,
+                     int64_t B, int64_t H, int64_t T, int64_t d, int causal, float scale,
+                     hipStream_t stream) {
+  return attn_bwd_gqa(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, H, T, d, causal, scale,
+                      stream);
 }
 
 const char* attn_bwd_kernel_name(int64_t d, int causal, int which) {

@@ -97,14 +97,24 @@ __host__ __device__ constexpr int acc_key_plain(int r, int h) {
   return 8 * (r / 4) + 4 * h + (r & 3);
 }
 
-// Workgroup id -> (head index bh, query block qb).  Heavy-first: the
-// highest query blocks (most key tiles under a causal mask) get the lowest
-// ids.  Within a block index, ids walk the heads, so id and id + BH*k fall
-// on the same XCD whenever BH is a multiple of 8.
-__device__ __forceinline__ void block_coords(int BH, int nqb, int& bh, int& qb) {
+// Workgroup id -> (query head bhq, key/value head bhkv, query block qb).
+// Heavy-first: the highest query blocks (most key tiles under a causal mask)
+// get the lowest ids.  Within a block index, ids walk the heads so that id
+// and id + BH*k fall on the same XCD whenever BH is a multiple of 8
+// (workgroups are dispatched round-robin over the 8 XCDs).  With grouped
+// key/value heads (G query heads per key/value head, "FlashAttention --
+// avoid writing the giant intermediate", the closing note on grouped-query
+// attention), head slot hid maps to member hid / NKV of group hid % NKV, so
+// the G query heads that read one key/value head also share an XCD and its
+// L2 whenever NKV = BH / G is a multiple of 8.  G = 1 is the identity.
+__device__ __forceinline__ void block_coords(int BH, int nqb, int G, int& bhq, int& bhkv,
+                                             int& qb) {
   const int id = blockIdx.x;
   qb = nqb - 1 - id / BH;
-  bh = id % BH;
+  const int hid = id % BH;
+  const int nkv = BH / G;
+  bhkv = hid % nkv;
+  bhq = bhkv * G + hid / nkv;
 }
 
 // Max of x over the lane pair (l, l ^ 32) that holds one query's scores.
@@ -249,7 +259,7 @@ __device__ __forceinline__ float sum_tree(const float* x) {
 template <int D, bool CAUSAL, bool PRESCALE>
 __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, float c) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, int G, float c) {
   using C = Bf16Tile<D>;
   constexpr int NW = C::NW, BC = C::BC, NDS = C::NDS, NDT = C::NDT;
   constexpr int RB = C::RB, NCH = C::NCH, KSLOT = C::KSLOT, KROWB = C::KROWB;
@@ -273,12 +283,13 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, h = lane >> 5;
-  int bh, qb;
-  block_coords(BH, nqb, bh, qb);
+  int bh, bhkv, qb;
+  block_coords(BH, nqb, G, bh, bhkv, qb);
   const size_t head = (size_t)bh * (size_t)T * D;
+  const size_t kvhead = (size_t)bhkv * (size_t)T * D;
   const int head_bytes = T * RB;
-  const __bf16* Kh = K + head;
-  const __bf16* Vh = V + head;
+  const __bf16* Kh = K + kvhead;
+  const __bf16* Vh = V + kvhead;
   const int q0 = qb * kBRBf16;
   const int qg = q0 + wave * 32 + j;
 
@@ -624,7 +635,7 @@ struct F32Tile {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, float c) {
+    float* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, int G, float c) {
   using C = F32Tile<D>;
   constexpr int BC = C::BC, NDS = C::NDS, NDT = C::NDT, KS = C::KS, VS = C::VS;
   constexpr int CH = C::CH, DCH = C::DCH;
@@ -636,12 +647,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, h = lane >> 5;
-  int bh, qb;
-  block_coords(BH, nqb, bh, qb);
+  int bh, bhkv, qb;
+  block_coords(BH, nqb, G, bh, bhkv, qb);
   const size_t head = (size_t)bh * (size_t)T * D;
+  const size_t kvhead = (size_t)bhkv * (size_t)T * D;
   const float* Qh = Q + head;
-  const float* Kh = K + head;
-  const float* Vh = V + head;
+  const float* Kh = K + kvhead;
+  const float* Vh = V + kvhead;
   const int q0 = qb * kBR;
   const int q0w = q0 + wave * 32;
   const int qg = q0w + j;
@@ -758,13 +770,15 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 }
 
 attn_status validate(const void* q, const void* k, const void* v, const void* o, const void* lse,
-                     int64_t B, int64_t H, int64_t T, int64_t d, int causal, float scale,
-                     int64_t elem, bool& empty) {
+                     int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t d, int causal,
+                     float scale, int64_t elem, bool& empty) {
   empty = false;
-  if (B < 0 || H < 0 || T < 0) return ATTN_ERR_SHAPE;
+  if (B < 0 || H < 0 || T < 0 || Hkv < 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return ATTN_ERR_ARG;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  // H is a whole number of groups of query heads per key/value head
+  if ((Hkv == 0) != (H == 0) || (Hkv > 0 && H % Hkv != 0)) return ATTN_ERR_SHAPE;
   if (B == 0 || H == 0 || T == 0) {
     empty = true;
     return ATTN_OK;
@@ -780,9 +794,9 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
   if (BH > (INT64_MAX / 8) / (T * d * elem)) return ATTN_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return ATTN_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return ATTN_ERR_ALIGN;
-  const int64_t nb = BH * T * d * elem, lb = BH * T * 4;
-  if (overlaps(o, nb, q, nb) || overlaps(o, nb, k, nb) || overlaps(o, nb, v, nb) ||
-      overlaps(lse, lb, q, nb) || overlaps(lse, lb, k, nb) || overlaps(lse, lb, v, nb) ||
+  const int64_t nb = BH * T * d * elem, kb = B * Hkv * T * d * elem, lb = BH * T * 4;
+  if (overlaps(o, nb, q, nb) || overlaps(o, nb, k, kb) || overlaps(o, nb, v, kb) ||
+      overlaps(lse, lb, q, nb) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) ||
       overlaps(lse, lb, o, nb))
     return ATTN_ERR_ARG;
   return ATTN_OK;
@@ -806,15 +820,15 @@ attn_status check_device() {
 }
 
 // Launches one workgroup of `threads` threads per `rows` query rows of each
-// head.
+// query head; G query heads share one key/value head.
 template <typename Elem>
 attn_status launch(const void* kernel, int threads, int rows, const Elem* q, const Elem* k,
-                   const Elem* v, Elem* o, float* lse, int64_t B, int64_t H, int64_t T,
-                   float scale, hipStream_t stream) {
-  int t = (int)T, bh = (int)(B * H), nqb = (int)((T + rows - 1) / rows);
+                   const Elem* v, Elem* o, float* lse, int64_t B, int64_t H, int64_t Hkv,
+                   int64_t T, float scale, hipStream_t stream) {
+  int t = (int)T, bh = (int)(B * H), nqb = (int)((T + rows - 1) / rows), g = (int)(H / Hkv);
   float c = scale * kLog2e;
-  void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&lse,
-                  (void*)&t, (void*)&bh,  (void*)&nqb, (void*)&c};
+  void* args[] = {(void*)&q, (void*)&k,   (void*)&v, (void*)&o, (void*)&lse,
+                  (void*)&t, (void*)&bh,  (void*)&nqb, (void*)&g, (void*)&c};
   const dim3 grid((unsigned)(bh * nqb)), block(threads);
   if (hipLaunchKernel(kernel, grid, block, args, 0, stream) != hipSuccess) return ATTN_ERR_LAUNCH;
   return ATTN_OK;
@@ -843,26 +857,32 @@ const void* f32_kernel(int64_t d, int causal) {
 
 extern "C" {
 
-attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                     int64_t H, int64_t T, int64_t d, int causal, float scale,
-                     hipStream_t stream) {
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t T, int64_t d, int causal,
+                         float scale, hipStream_t stream) {
   bool empty;
-  attn_status st = validate(q, k, v, o, lse, B, H, T, d, causal, scale, 2, empty);
+  attn_status st = validate(q, k, v, o, lse, B, H, H_kv, T, d, causal, scale, 2, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
   return launch<__bf16>(bf16_kernel(d, causal, scale), kThreadsBf16, kBRBf16, (const __bf16*)q,
-                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, B, H, T, scale,
-                        stream);
+                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, B, H, H_kv, T,
+                        scale, stream);
+}
+
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                     int64_t H, int64_t T, int64_t d, int causal, float scale,
+                     hipStream_t stream) {
+  return attn_fwd_gqa(q, k, v, o, lse, B, H, H, T, d, causal, scale, stream);
 }
 
 attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                          int64_t B, int64_t H, int64_t T, int64_t d, int causal, float scale,
                          hipStream_t stream) {
   bool empty;
-  attn_status st = validate(q, k, v, o, lse, B, H, T, d, causal, scale, 4, empty);
+  attn_status st = validate(q, k, v, o, lse, B, H, H, T, d, causal, scale, 4, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  return launch<float>(f32_kernel(d, causal), kThreads, kBR, q, k, v, o, lse, B, H, T, scale,
+  return launch<float>(f32_kernel(d, causal), kThreads, kBR, q, k, v, o, lse, B, H, H, T, scale,
                        stream);
 }
 

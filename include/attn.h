@@ -1,6 +1,7 @@
 /*
  * attn.h -- C ABI of the fused, I/O-aware forward pass of exact scaled
- * dot-product attention on AMD Instinct MI355X (gfx950).
+ * dot-product attention on AMD Instinct MI355X (gfx950), with its backward
+ * pass and grouped-query variants of both.
  *
  * For every (batch b, head h) the library computes, for queries Q, keys K
  * and values V of shape T x d,
@@ -29,12 +30,14 @@
  * [B][H][T] float array.  All pointers are device pointers.
  *
  * Ownership.  The caller owns every buffer.  The library allocates, frees
- * and keeps no device memory and uses no workspace.  It holds no mutable
- * state other than a per-device cache of the architecture check, and may be
- * called from several host threads.
+ * and keeps no device memory; the forward uses no workspace, the backward a
+ * caller-owned one (ws).  It holds no mutable state other than a per-device
+ * cache of the architecture check, and may be called from several host
+ * threads.
  *
- * Asynchrony.  Calls enqueue one kernel on `stream` (NULL = the null
- * stream) and return; they never synchronise.
+ * Asynchrony.  Calls enqueue their kernels (one for the forward, three for
+ * the backward) on `stream` (NULL = the null stream) and return; they never
+ * synchronise.
  *
  * Errors.  Arguments are validated on the host before any HIP call; on a
  * validation error nothing is launched and the outputs are untouched.  An
@@ -82,6 +85,23 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o,
                      int causal, float scale, hipStream_t stream);
 
 /*
+ * Grouped-query forward ("FlashAttention -- avoid writing the giant
+ * intermediate", closing note: grouped-query attention changes the head
+ * structure of the stored keys and values).  H query heads share H_kv
+ * key/value heads, G = H / H_kv query heads per key/value head: query head h
+ * reads key/value head h / G (consecutive query heads form a group).
+ * q, o: [B][H][T][d]; k, v: [B][H_kv][T][d]; lse: [B][H][T].  H_kv >= 1
+ * must divide H (H_kv = H is attn_fwd; H_kv = 1 is multi-query attention);
+ * otherwise ATTN_ERR_SHAPE.  Everything else as for attn_fwd.  Workgroups of
+ * one group are placed on one XCD when B*H_kv is a multiple of 8, so the
+ * group's K/V tiles are fetched into one L2.
+ */
+attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
+                         float* lse, int64_t B, int64_t H, int64_t H_kv,
+                         int64_t T, int64_t d, int causal, float scale,
+                         hipStream_t stream);
+
+/*
  * float32 forward: the same contract with float elements in q, k, v, o.
  * Both contractions use fp32 MFMA (no reduced-precision inputs); P stays
  * fp32.
@@ -123,6 +143,18 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const void* dout, const float* lse, void* dq, void* dk,
                      void* dv, float* ws, int64_t B, int64_t H, int64_t T,
                      int64_t d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Grouped-query backward: the gradient of attn_fwd_gqa.  k, v, dk, dv are
+ * [B][H_kv][T][d]; dK and dV of a key/value head sum the contributions of
+ * its G query heads (accumulated in registers by one workgroup, no
+ * atomics).  Everything else as for attn_bwd (ws: 2*B*H*T floats).
+ */
+attn_status attn_bwd_gqa(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, float* ws, int64_t B,
+                         int64_t H, int64_t H_kv, int64_t T, int64_t d,
+                         int causal, float scale, hipStream_t stream);
 
 /*
  * Name of kernel `which` (0 = row statistics, 1 = dK/dV, 2 = dQ) that

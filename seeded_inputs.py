@@ -103,19 +103,22 @@ class QKV:
 
 
 def make_qkv(B: int, H: int, T: int, d: int, *, dtype: str = "bf16",
-             seed: int = 0, qk_mult: float = 1.0) -> QKV:
+             seed: int = 0, qk_mult: float = 1.0, H_kv: int | None = None) -> QKV:
     """Draw Q, K, V i.i.d. standard normal (float32) from PCG64(seed).
 
-    Draw order is Q, then K, then V.  Q and K are multiplied by ``qk_mult``
-    before rounding to bfloat16 (a power of two such as 4 commutes with the
-    rounding, so the order does not matter for it).
+    Draw order is Q, then K, then V.  Q is [B, H, T, d]; K and V are
+    [B, H_kv, T, d] (H_kv = H unless given: grouped key/value heads).  Q and
+    K are multiplied by ``qk_mult`` before rounding to bfloat16 (a power of
+    two such as 4 commutes with the rounding, so the order does not matter
+    for it).
     """
     if dtype not in ("bf16", "f32"):
         raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
+    H_kv = H if H_kv is None else H_kv
     rng = np.random.Generator(np.random.PCG64(seed))
-    shape = (B, H, T, d)
     arrs = []
     for name in ("q", "k", "v"):
+        shape = (B, H if name == "q" else H_kv, T, d)
         a = rng.standard_normal(shape, dtype=np.float32)
         if name in ("q", "k") and qk_mult != 1.0:
             a *= np.float32(qk_mult)
@@ -157,6 +160,9 @@ WORKLOADS = {
     "bf16_b1h32_t8192_d128_causal_qk4": dict(
         B=1, H=32, T=8192, d=128, dtype="bf16", causal=(True,), seed=4,
         qk_mult=4.0),
+    # grouped key/value heads: 32 query heads over 8 key/value heads
+    "bf16_b1h32kv8_t8192_d128_causal": dict(
+        B=1, H=32, H_kv=8, T=8192, d=128, dtype="bf16", causal=(True,), seed=6),
     "bf16_b1h8_t65536_d128_causal": dict(
         B=1, H=8, T=65536, d=128, dtype="bf16", causal=(True,), seed=5,
         sample_rows=512, row_seed=1005),
@@ -166,6 +172,6 @@ WORKLOADS = {
 def make_workload(name: str) -> QKV:
     w = WORKLOADS[name]
     x = make_qkv(w["B"], w["H"], w["T"], w["d"], dtype=w["dtype"],
-                 seed=w["seed"], qk_mult=w.get("qk_mult", 1.0))
+                 seed=w["seed"], qk_mult=w.get("qk_mult", 1.0), H_kv=w.get("H_kv"))
     x.meta = dict(w, name=name)
     return x

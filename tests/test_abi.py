@@ -154,3 +154,30 @@ def test_bwd_kernel_names_and_flops():
     assert ea.bwd_kernel_name(128, True, 3) is None
     # five T x T x d contractions: 2.5 times the forward
     assert ea.bwd_flops(1, 32, 8192, 128, True) == pytest.approx(2.5 * 549.755813888e9)
+
+
+@no_gpu_only
+def test_gqa_validation_errors():
+    def fwd(**kw):
+        a = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=8, Hkv=2, T=8, d=64,
+                 causal=1, scale=0.125)
+        a.update(kw)
+        return ea.attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                               a["Hkv"], a["T"], a["d"], a["causal"], a["scale"])
+    assert fwd(Hkv=3) == 2          # H not a multiple of H_kv
+    assert fwd(Hkv=0) == 2
+    assert fwd(Hkv=-1) == 2
+    assert fwd(Hkv=16) == 2
+    assert fwd(q=0) == 1
+    assert fwd(d=96) == 3
+    assert fwd(B=0, q=0, k=0, v=0, o=0, lse=0) == 0
+    assert fwd(H=0, Hkv=0, q=0, k=0, v=0, o=0, lse=0) == 0
+
+    def bwd(**kw):
+        a = dict(B=1, H=8, Hkv=2, T=8, d=64)
+        a.update(kw)
+        return ea.attn_bwd_gqa(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, 8 * A, 9 * A,
+                               10 * A, a["B"], a["H"], a["Hkv"], a["T"], a["d"], 1, 0.125)
+    assert bwd(Hkv=3) == 2
+    assert bwd(Hkv=0) == 2
+    assert bwd(d=32) == 3
