@@ -13,6 +13,9 @@ Contents
   backward         -- gradients dQ, dK, dV (and Delta) of the materialised
                       definition for an upstream gradient dO; pinned by
                       tests/test_oracle_bwd_pins.py.
+  decode           -- a few new queries over a key/value cache (queries at the
+                      last positions, bottom-right causal mask); pinned by
+                      tests/test_oracle_decode_pins.py.
   gqa              -- grouped key/value heads (query head h reads key/value
                       head h // (H / H_kv)) for the forward and the backward;
                       pinned by tests/test_oracle_gqa_pins.py.
@@ -33,5 +36,6 @@ an invariant or an independent brute force.
 """
 from .attention import attention, attention_head, attention_heads  # noqa: F401
 from .backward import attention_head_bwd  # noqa: F401
+from .decode import attention_decode, attention_decode_head  # noqa: F401
 from .gqa import attention_gqa, attention_gqa_bwd, kv_head  # noqa: F401
 from .online_model import online_attention_head, tile_local_softmax_head  # noqa: F401
