@@ -20,7 +20,8 @@ import os
 
 __all__ = [
     "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_fwd_gqa",
-    "attn_bwd_gqa", "kernel_name",
+    "attn_bwd_gqa", "attn_decode", "decode", "decode_workspace_bytes", "decode_splits",
+    "kernel_name",
     "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
     "LIB_PATH", "STATUS", "flops", "bwd_flops",
 ]
@@ -30,7 +31,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
     4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_ALIGN", 6: "ATTN_ERR_ARG", 7: "ATTN_ERR_DEVICE",
-    8: "ATTN_ERR_LAUNCH",
+    8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_WORKSPACE",
 }
 
 # The C prototypes from include/attn.h.
@@ -45,6 +46,10 @@ EXPORTS = {
                      + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_bwd_gqa": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5
                      + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_decode": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 8
+                    + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_decode_workspace_bytes": (ctypes.c_int64, [ctypes.c_int64] * 6),
+    "attn_decode_splits": (ctypes.c_int64, [ctypes.c_int64] * 3),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_kernel_name": (ctypes.c_char_p, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
@@ -127,6 +132,21 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, T, d, causal, scale,
     status."""
     return load_library().attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, T, d,
                                    int(causal), float(scale), stream or None)
+
+
+def attn_decode(q, k, v, o, lse, ws, ws_bytes, B, H, H_kv, Tq, Tk, Tk_cap, d, causal, scale,
+                stream=0) -> int:
+    """Raw decode entry point: integer device addresses, returns the status."""
+    return load_library().attn_decode(q, k, v, o, lse, ws or None, ws_bytes, B, H, H_kv, Tq, Tk,
+                                      Tk_cap, d, int(causal), float(scale), stream or None)
+
+
+def decode_workspace_bytes(B: int, H: int, H_kv: int, Tq: int, Tk: int, d: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, H, H_kv, Tq, Tk, d))
+
+
+def decode_splits(B: int, H_kv: int, Tk: int) -> int:
+    return int(load_library().attn_decode_splits(B, H_kv, Tk))
 
 
 def flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
@@ -237,3 +257,43 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
     if st != 0:
         raise AttnError(st, status_string(st))
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, Tk: int | None = None, causal: bool = True,
+           scale: float | None = None, out=None, lse=None, ws=None, stream=None):
+    """Decode on bf16 torch tensors: q [B, H, Tq, d] (the last Tq positions),
+    k_cache, v_cache [B, H_kv, Tk_cap, d] with the first ``Tk`` rows valid
+    (default all).  Returns (o [B, H, Tq, d] bf16, lse [B, H, Tq] float32).
+    ``ws`` is an optional uint8/any-dtype device buffer of at least
+    decode_workspace_bytes(...) bytes (allocated when None and needed)."""
+    import torch
+
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, H, Tq, d] and the caches [B, H_kv, Tk_cap, d]")
+    B, H, Tq, d = q.shape
+    Hkv, Tcap = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("cache batch and head dimension must match q")
+    if any(t.dtype != torch.bfloat16 for t in (q, k_cache, v_cache)):
+        raise ValueError("decode takes bfloat16 tensors")
+    for t in (q, k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q and the caches must be contiguous CUDA tensors")
+    Tk = Tcap if Tk is None else int(Tk)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_workspace_bytes(B, H, Hkv, Tq, Tk, d) if Hkv and Tk else 0
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ws.data_ptr() if ws is not None else 0
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    with torch.cuda.device(q.device):
+        st = attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), ws_ptr, ws_bytes, B, H, Hkv, Tq, Tk, Tcap, d, causal,
+                         scale, s)
+    if st != 0:
+        raise AttnError(st, status_string(st))
+    return out, lse

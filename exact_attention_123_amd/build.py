@@ -2,8 +2,8 @@
 
     python -m exact_attention_123_amd.build
 
-compiles ``csrc/attn_fwd.hip`` (forward) and ``csrc/attn_bwd.hip`` (backward)
-with hipcc into
+compiles ``csrc/attn_fwd.hip`` (forward), ``csrc/attn_bwd.hip`` (backward) and
+``csrc/attn_decode.hip`` (decode over a key/value cache) with hipcc into
 ``exact_attention_123_amd/libattn.so``.  The library exports the C ABI of
 ``include/attn.h``; the Python binding loads it with ctypes.
 """
@@ -16,7 +16,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 

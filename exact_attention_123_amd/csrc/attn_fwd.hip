@@ -897,6 +897,7 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_ARG: return "causal must be 0 or 1 and outputs must not overlap any buffer";
     case ATTN_ERR_DEVICE: return "current device is not an AMD gfx950 GPU";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than required";
   }
   return "unknown status";
 }

@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of the fused, I/O-aware forward pass of exact scaled
  * dot-product attention on AMD Instinct MI355X (gfx950), with its backward
- * pass and grouped-query variants of both.
+ * pass, grouped-query variants of both, and decode over a key/value cache.
  *
  * For every (batch b, head h) the library computes, for queries Q, keys K
  * and values V of shape T x d,
@@ -30,14 +30,14 @@
  * [B][H][T] float array.  All pointers are device pointers.
  *
  * Ownership.  The caller owns every buffer.  The library allocates, frees
- * and keeps no device memory; the forward uses no workspace, the backward a
- * caller-owned one (ws).  It holds no mutable state other than a per-device
+ * and keeps no device memory; the forward uses no workspace, the backward and
+ * the decode a caller-owned one (ws).  It holds no mutable state other than a per-device
  * cache of the architecture check, and may be called from several host
  * threads.
  *
  * Asynchrony.  Calls enqueue their kernels (one for the forward, three for
- * the backward) on `stream` (NULL = the null stream) and return; they never
- * synchronise.
+ * the backward, one or two for the decode) on `stream` (NULL = the null
+ * stream) and return; they never synchronise.
  *
  * Errors.  Arguments are validated on the host before any HIP call; on a
  * validation error nothing is launched and the outputs are untouched.  An
@@ -56,13 +56,14 @@ extern "C" {
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a pointer is NULL for a non-empty problem      */
-  ATTN_ERR_SHAPE = 2,       /* B, H or T negative, or sizes overflow limits   */
+  ATTN_ERR_SHAPE = 2,       /* sizes negative, inconsistent or over limits    */
   ATTN_ERR_UNSUPPORTED = 3, /* head dimension d is not 64 or 128              */
   ATTN_ERR_SCALE = 4,       /* scale is NaN or infinite                       */
   ATTN_ERR_ALIGN = 5,       /* q/k/v/o not 16-byte or lse not 4-byte aligned  */
   ATTN_ERR_ARG = 6,         /* causal not 0/1, or an output overlaps a buffer */
   ATTN_ERR_DEVICE = 7,      /* the current device is not gfx950               */
-  ATTN_ERR_LAUNCH = 8       /* the HIP runtime reported an error at launch    */
+  ATTN_ERR_LAUNCH = 8,      /* the HIP runtime reported an error at launch    */
+  ATTN_ERR_WORKSPACE = 9    /* the workspace is missing or too small          */
 } attn_status;
 
 /*
@@ -162,6 +163,48 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v,
  * "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4".  NULL if unsupported.
  */
 const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
+
+/*
+ * Decode: Tq new queries per head over a key/value cache ("FlashAttention --
+ * avoid writing the giant intermediate": short-input decode against the
+ * stored key/value state, as opposed to long-input prefill).  The queries
+ * are the last Tq positions of the cached sequence: query i sits at
+ * position Tk - Tq + i and, with causal = 1, sees keys j <= Tk - Tq + i
+ * (without the mask, all Tk keys).  O and LSE are defined as for the
+ * forward.
+ *   q, o:  __hip_bfloat16 [B][H][Tq][d];  lse: float [B][H][Tq];
+ *   k, v:  const __hip_bfloat16 caches [B][H_kv][Tk_cap][d] of which rows
+ *          0 .. Tk-1 of each head are valid (rows >= Tk are never read);
+ *   H_kv divides H, query head h reads key/value head h / (H / H_kv);
+ *   Tq * (H / H_kv) <= 32 (more new queries per key/value head are a
+ *          prefill: ATTN_ERR_UNSUPPORTED);  1 <= Tk <= Tk_cap, and Tk >= Tq
+ *          when causal (ATTN_ERR_SHAPE otherwise);
+ *   ws, ws_bytes: caller-owned device workspace of at least
+ *          attn_decode_workspace_bytes(B, H, H_kv, Tq, Tk, d) bytes,
+ *          16-byte aligned (may be NULL when that is 0), overwritten.  Too
+ *          small: ATTN_ERR_WORKSPACE.
+ * The keys are split into attn_decode_splits(B, H_kv, Tk) consecutive
+ * ranges, one workgroup each, whose partial results (normalised output and
+ * LSE per query row, fp32, in ws) a second kernel merges as
+ * LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  The query heads
+ * of one key/value head are processed together, so the cache is read once
+ * per group.  Two kernels are enqueued (one when there is a single split).
+ * Other arguments and errors as for attn_fwd.
+ */
+attn_status attn_decode(const void* q, const void* k, const void* v, void* o,
+                        float* lse, void* ws, int64_t ws_bytes, int64_t B,
+                        int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                        int64_t Tk_cap, int64_t d, int causal, float scale,
+                        hipStream_t stream);
+
+/* Workspace bytes attn_decode needs for these sizes (0 if none, or if the
+ * sizes are invalid). */
+int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv,
+                                    int64_t Tq, int64_t Tk, int64_t d);
+
+/* Number of key ranges attn_decode splits each key/value head into
+ * (0 if the sizes are invalid). */
+int64_t attn_decode_splits(int64_t B, int64_t H_kv, int64_t Tk);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_string(attn_status s);

@@ -27,6 +27,8 @@ __all__ = [
     "sample_rows",
     "make_workload",
     "make_dout",
+    "make_decode",
+    "DECODE_WORKLOADS",
 ]
 
 
@@ -175,3 +177,41 @@ def make_workload(name: str) -> QKV:
                  seed=w["seed"], qk_mult=w.get("qk_mult", 1.0), H_kv=w.get("H_kv"))
     x.meta = dict(w, name=name)
     return x
+
+
+# ---------------------------------------------------------------------------
+# Decode: new queries over a key/value cache
+# ---------------------------------------------------------------------------
+
+def make_decode(B: int, H: int, H_kv: int, Tq: int, Tk: int, d: int, *, seed: int,
+                Tk_cap: int | None = None, qk_mult: float = 1.0) -> QKV:
+    """Draw the Tq new queries [B, H, Tq, d] and caches [B, H_kv, Tk_cap, d]
+    i.i.d. standard normal (float32) from PCG64(seed), in the order Q, K, V,
+    rounded to bfloat16.  Cache rows >= Tk (capacity beyond the valid
+    length) hold the bit pattern 0x7FC0 (a NaN), which no correct reader
+    touches."""
+    Tk_cap = Tk if Tk_cap is None else Tk_cap
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, H, Tq, d), dtype=np.float32)
+    k = rng.standard_normal((B, H_kv, Tk, d), dtype=np.float32)
+    v = rng.standard_normal((B, H_kv, Tk, d), dtype=np.float32)
+    if qk_mult != 1.0:
+        q *= np.float32(qk_mult)
+        k *= np.float32(qk_mult)
+    arrs = [f32_to_bf16_bits(q)]
+    for a in (k, v):
+        full = np.full((B, H_kv, Tk_cap, d), 0x7FC0, dtype=np.uint16)
+        full[:, :, :Tk] = f32_to_bf16_bits(a)
+        arrs.append(full)
+    return QKV(dtype="bf16", q=arrs[0], k=arrs[1], v=arrs[2], seed=seed, qk_mult=qk_mult,
+               meta=dict(B=B, H=H, H_kv=H_kv, Tq=Tq, Tk=Tk, Tk_cap=Tk_cap, d=d))
+
+
+# Decode workloads: one new token per sequence over a long cache, grouped
+# key/value heads (32 query heads over 8 key/value heads).
+DECODE_WORKLOADS = {
+    "bf16_b16h32kv8_tq1_tk32768_d128_causal": dict(
+        B=16, H=32, H_kv=8, Tq=1, Tk=32768, d=128, causal=True, seed=8),
+    "bf16_b1h32kv8_tq1_tk131072_d128_causal": dict(
+        B=1, H=32, H_kv=8, Tq=1, Tk=131072, d=128, causal=True, seed=9),
+}

@@ -181,3 +181,40 @@ def test_gqa_validation_errors():
     assert bwd(Hkv=3) == 2
     assert bwd(Hkv=0) == 2
     assert bwd(d=32) == 3
+
+
+@no_gpu_only
+def test_decode_validation_errors():
+    def dec(**kw):
+        a = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, ws=6 * A, wsb=1 << 30, B=1, H=8,
+                 Hkv=2, Tq=1, Tk=100, Tcap=100, d=128, causal=1, scale=0.1)
+        a.update(kw)
+        return ea.attn_decode(a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"], a["wsb"],
+                              a["B"], a["H"], a["Hkv"], a["Tq"], a["Tk"], a["Tcap"], a["d"],
+                              a["causal"], a["scale"])
+    assert dec(Hkv=3) == 2                 # H not a multiple of H_kv
+    assert dec(Tk=0) == 2                  # a query needs a key
+    assert dec(Tq=3, Tk=2, Tcap=2) == 2    # causal: the queries are cache positions
+    assert dec(Tcap=50) == 2               # valid length beyond capacity
+    assert dec(Tq=9) == 3                  # 9 * 4 rows > 32 per key/value head
+    assert dec(d=96) == 3
+    assert dec(q=0) == 1
+    assert dec(causal=2) == 6
+    assert dec(o=A) == 6
+    assert dec(Tq=0) == 0                  # nothing to do
+    # the split needs a workspace here
+    assert ea.decode_workspace_bytes(1, 8, 2, 1, 100000, 128) > 0
+    far = dict(Tk=100000, Tcap=100000, q=1 << 36, k=2 << 36, v=3 << 36, o=4 << 36,
+               lse=5 << 36)
+    assert dec(ws=0, wsb=0, **far) == 9
+    assert dec(ws=6 << 36, wsb=16, **far) == 9
+
+
+def test_decode_split_sizes():
+    # enough splits to fill the chip, each at least 256 keys
+    assert ea.decode_splits(1, 8, 131072) == 128
+    assert ea.decode_splits(16, 8, 32768) == 8
+    assert ea.decode_splits(1, 1, 100) == 1
+    assert ea.decode_splits(2048, 8, 4096) == 1
+    assert ea.decode_workspace_bytes(2048, 32, 8, 1, 4096, 128) == 0
+    assert ea.decode_workspace_bytes(1, 32, 8, 1, 131072, 128) == 128 * 32 * 129 * 4
