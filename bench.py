@@ -12,12 +12,26 @@ dQ kernels) on the same workload with a seeded upstream gradient dO, after
 one untimed forward that provides O and LSE.  FLOPs counted: the five T x T x
 d contractions of the gradient, 2.5 times the forward's count.
 
+``--pass decode``: one step = one decode call (split-KV kernel and, with
+several splits, the merge kernel) of the new queries over a key/value cache;
+default workload B=16 sequences, 32 query heads over 8 key/value heads, one
+new query each, 32768 cached keys, d=128.  The path reads the cache once, so
+it is HBM-bound: the value is GB/s of algorithmic bytes (the valid cache
+rows of K and V, Q, O, LSE) against MI355X's 8 TB/s.
+
+``--pass mat``: one step = one call of the materialised three-kernel forward
+(S in fp32 and P in bf16 written to and read back from device memory) on the
+default forward workload; same FLOP count as the fused forward.  It is
+HBM-bound: the roofline is GB/s of the S and P traffic (plus Q, K, V, O, LSE)
+against 8 TB/s, and the fused forward is timed in the same run for the
+comparison.
+
 Prints one JSON line with the throughput, the roofline position of the pass
 (MFMA-bound, against MI355X's dense bf16 peak; for the backward the three
 kernels of one call are timed together) and the float64 CPU oracle timed on a
 bounded sample of the same workload on this host's cores.
 
-    python bench.py [--pass fwd|bwd] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--pass fwd|bwd|decode|mat] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -34,6 +48,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "bf16_b1h32_t8192_d128_causal_qk4"
+DEFAULT_DECODE_WORKLOAD = "bf16_b16h32kv8_tq1_tk32768_d128_causal"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 # MI355X published dense peaks (TFLOP/s) by MFMA input type.
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 PROFILES = os.path.join(ROOT, "profiles")
@@ -106,17 +122,277 @@ def cpu_baseline(x, causal: bool, scale: float, heads: int, pass_: str, do_bits=
     }
 
 
+def time_steps(step, stream, steps: int, warmup: int):
+    """W untimed steps, then K steps between HIP events on the launch
+    stream.  Returns (per-step ms list, region ms, wall s)."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return per, starts[0].elapsed_time(ends[-1]), wall
+
+
+def copy_calibration(mib: int, dev):
+    """One plain device-to-device copy of `mib` MiB (counter calibration)."""
+    import torch
+
+    if mib:
+        n = mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+
+def run_decode(args) -> int:
+    import numpy as np
+    import torch
+
+    import exact_attention_123_amd as ea
+    import oracle
+    from seeded_inputs import DECODE_WORKLOADS, bf16_bits_to_f32, make_decode
+
+    name = args.workload or DEFAULT_DECODE_WORKLOAD
+    w = DECODE_WORKLOADS[name]
+    B, H, Hkv, Tq, Tk, d, causal = (w[k] for k in ("B", "H", "H_kv", "Tq", "Tk", "d", "causal"))
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_decode(B, H, Hkv, Tq, Tk, d, seed=w["seed"])
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=dev)
+    need = ea.decode_workspace_bytes(B, H, Hkv, Tq, Tk, d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+    def step():
+        ea.decode(q, k, v, Tk=Tk, causal=causal, scale=scale, out=out, lse=lse, ws=ws)
+
+    def ref_head(b, h):
+        g = h // G
+        return oracle.attention_decode_head(
+            bf16_bits_to_f32(x.q[b, h]).astype(np.float64),
+            bf16_bits_to_f32(x.k[b, g, :Tk]).astype(np.float64),
+            bf16_bits_to_f32(x.v[b, g, :Tk]).astype(np.float64), causal=causal, scale=scale)
+
+    parity = None
+    if not args.no_parity:
+        step()
+        torch.cuda.synchronize()
+        O = bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16))
+        L = lse.cpu().numpy()
+        eo = el = 0.0
+        heads = [(0, 0), (0, H - 1), (B - 1, 0), (B - 1, H - 1)]
+        for (b, h) in heads:
+            r = ref_head(b, h)
+            eo = max(eo, float(np.abs(O[b, h] - r["O"]).max()))
+            el = max(el, float(np.abs(L[b, h] - r["LSE"]).max()))
+        parity = {"heads_checked": len(heads), "max_abs_err_o": eo, "max_abs_err_lse": el,
+                  "pass": bool(eo <= 2e-2 and el <= 1e-3)}
+        if not parity["pass"]:
+            print(json.dumps({"error": "parity failed", "parity": parity}), flush=True)
+            return 1
+
+    stream = torch.cuda.current_stream(dev)
+    per, region_ms, wall = time_steps(step, stream, args.steps, args.warmup)
+    copy_calibration(args.copy_calibration_mib, dev)
+    ms_per_step = region_ms / args.steps
+    avg_ms = sum(per) / len(per)
+    nbytes = (2 * B * Hkv * Tk * d * 2      # valid K and V cache rows, read once
+              + 2 * B * H * Tq * d * 2      # Q read, O written
+              + B * H * Tq * 4)             # LSE written
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    kname = f"attn_decode_bf16_d{d}_{'causal' if causal else 'full'}_w4_blk32"
+    traffic = measured_traffic(kname, name, "decode")
+    res = {
+        "metric": f"decode attn GB/s (bf16, Tq={Tq}, Tk={Tk}, d={d}) + % HBM peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded PCG64 N(0,1) draws rounded to bf16 (RNE)",
+        "config": {"workload": name, "pass": "decode", "B": B, "H": H, "H_kv": Hkv, "Tq": Tq,
+                   "Tk": Tk, "d": d, "causal": causal, "scale": scale,
+                   "splits": ea.decode_splits(B, Hkv, Tk), "bytes_per_step": nbytes,
+                   "kernel": kname, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "timing": {"avg_launch_ms": round(avg_ms, 4), "min_launch_ms": round(min(per), 4),
+                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3)},
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        seqs = args.cpu_heads if args.cpu_heads is not None else 2
+        t0 = time.perf_counter()
+        done = 0
+        for b in range(min(seqs, B)):
+            for h in range(H):
+                ref_head(b, h)
+            done += 1
+        dt = time.perf_counter() - t0
+        cb = done * (2 * Hkv * Tk * d * 2 + 2 * H * Tq * d * 2 + H * Tq * 4)
+        res["cpu_baseline"] = {
+            "value": cb / dt / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} of {B} sequences, all {H} query heads each; float64 numpy, "
+                      f"scores and probabilities materialised; {dt:.1f} s wall",
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def mat_bytes(B: int, H: int, T: int, d: int, causal: bool) -> int:
+    """Algorithmic bytes of one materialised forward: S written (fp32) and
+    read once over each row's visible part, P written and read (bf16) over
+    the tiles the kernels touch, Q, K, V read once, O and LSE written."""
+    R = 128  # query rows per block of the scores and P V kernels
+    if causal:
+        nqb = T // R
+        touched = R * R * nqb * (nqb + 1) // 2  # entries of the blocks' key ranges
+        visible = T * (T + 1) // 2
+    else:
+        touched = visible = T * T
+    per_head = touched * 4 + visible * 4 + 2 * touched * 2 + 4 * T * d * 2 + T * 4
+    return B * H * per_head
+
+
+def run_mat(args) -> int:
+    import numpy as np
+    import torch
+
+    import exact_attention_123_amd as ea
+    import oracle
+    from seeded_inputs import WORKLOADS, bf16_bits_to_f32, make_workload
+
+    name = args.workload or DEFAULT_WORKLOAD
+    w = WORKLOADS[name]
+    causal = w["causal"][0]
+    B, H, T, d = w["B"], w["H"], w["T"], w["d"]
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_workload(name)
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    s_buf = torch.empty((B, H, T, T), dtype=torch.float32, device=dev)
+    p_buf = torch.empty((B, H, T, T), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ea.forward_materialized(q, k, v, causal=causal, scale=scale, out=out, lse=lse,
+                                s_buf=s_buf, p_buf=p_buf)
+
+    parity = None
+    if not args.no_parity:
+        step()
+        torch.cuda.synchronize()
+        O = bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16))
+        L = lse.cpu().numpy()
+        rows = np.unique(np.r_[0, 1, 127, 128, T // 2, T - 1,
+                               np.random.Generator(np.random.PCG64(9)).choice(T, 24)])
+        eo = el = 0.0
+        for (b, h) in ((0, 0), (B - 1, H - 1)):
+            ref = oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h), causal=causal,
+                                        scale=scale, rows=rows)
+            eo = max(eo, float(np.abs(O[b, h][rows] - ref["O"]).max()))
+            el = max(el, float(np.abs(L[b, h][rows] - ref["LSE"]).max()))
+        parity = {"rows_checked": int(2 * len(rows)), "max_abs_err_o": eo,
+                  "max_abs_err_lse": el, "pass": bool(eo <= 2e-2 and el <= 1e-3)}
+        if not parity["pass"]:
+            print(json.dumps({"error": "parity failed", "parity": parity}), flush=True)
+            return 1
+
+    stream = torch.cuda.current_stream(dev)
+    steps = max(1, args.steps // 10)  # each step moves ~13 GB: a tenth of the steps
+    warm = max(1, args.warmup // 10)
+    per, region_ms, wall = time_steps(step, stream, steps, warm)
+    o2 = torch.empty_like(q)
+    l2 = torch.empty_like(lse)
+    fper, _, _ = time_steps(lambda: ea.forward(q, k, v, causal=causal, scale=scale, out=o2,
+                                               lse=l2), stream, steps, warm)
+    copy_calibration(args.copy_calibration_mib, dev)
+    ms_per_step = region_ms / steps
+    avg_ms = sum(per) / len(per)
+    fused_ms = sum(fper) / len(fper)
+    fl = ea.flops(B, H, T, d, causal)
+    nbytes = mat_bytes(B, H, T, d, causal)
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    kname = f"attn_mat_bf16_d{d}_{'causal' if causal else 'full'}_3k"
+    res = {
+        "metric": (f"materialised {'causal ' if causal else ''}attn fwd TFLOP/s (bf16, T={T}, "
+                   f"d={d}) + % HBM peak"),
+        "value": round(fl / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded PCG64 N(0,1) draws rounded to bf16 (RNE)"
+                + (", Q and K multiplied by 4" if w.get("qk_mult", 1.0) != 1.0 else ""),
+        "config": {"workload": name, "pass": "mat", "B": B, "H": H, "T": T, "d": d,
+                   "causal": causal, "scale": scale, "flops_per_step": fl,
+                   "bytes_per_step": nbytes, "s_dtype": "f32", "p_dtype": "bf16",
+                   "kernel": kname, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(kname, name, "mat")},
+        "timing": {"avg_launch_ms": round(avg_ms, 4), "min_launch_ms": round(min(per), 4),
+                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3)},
+        "compare": {"fused_fwd_avg_ms": round(fused_ms, 4),
+                    "materialised_over_fused": round(avg_ms / fused_ms, 2)},
+        "parity": parity,
+    }
+    if not args.no_cpu_baseline:
+        heads = args.cpu_heads if args.cpu_heads is not None else 32
+        res["cpu_baseline"] = cpu_baseline(x, causal, scale, min(heads, B * H), "fwd")
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd"], default="fwd")
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "decode", "mat"],
+                    default="fwd")
+    ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=None,
-                    help="heads of the workload the CPU oracle is timed on "
-                         "(default 32 for fwd, 2 for bwd)")
+                    help="heads (fwd, bwd) or sequences (decode) of the workload the CPU "
+                         "oracle is timed on (default 32 for fwd, 2 for bwd and decode)")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (for counter calibration)")
@@ -128,6 +404,12 @@ def main() -> int:
               "(heads shard across GPUs with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.pass_ == "decode":
+        return run_decode(args)
+    if args.pass_ == "mat":
+        return run_mat(args)
+    args.workload = args.workload or DEFAULT_WORKLOAD
 
     import numpy as np
     import torch
@@ -227,33 +509,10 @@ def main() -> int:
             return 1
 
     stream = torch.cuda.current_stream(dev)  # the launch stream of the binding
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region: events on the launch stream around each call.
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    region_ms = starts[0].elapsed_time(ends[-1])
+    per_launch_ms, region_ms, wall = time_steps(step, stream, args.steps, args.warmup)
     ms_per_step = region_ms / args.steps
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
-
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        bcopy = torch.empty_like(a)
-        bcopy.copy_(a)
-        torch.cuda.synchronize()
+    copy_calibration(args.copy_calibration_mib, dev)
 
     value = fl / (ms_per_step * 1e-3) / 1e12
     achieved = fl / (avg_launch_ms * 1e-3) / 1e12

@@ -21,6 +21,7 @@ import os
 __all__ = [
     "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_fwd_gqa",
     "attn_bwd_gqa", "attn_decode", "decode", "decode_workspace_bytes", "decode_splits",
+    "attn_fwd_materialized", "forward_materialized",
     "kernel_name",
     "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
     "LIB_PATH", "STATUS", "flops", "bwd_flops",
@@ -50,6 +51,8 @@ EXPORTS = {
                     + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_decode_workspace_bytes": (ctypes.c_int64, [ctypes.c_int64] * 6),
     "attn_decode_splits": (ctypes.c_int64, [ctypes.c_int64] * 3),
+    "attn_fwd_materialized": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 4
+                              + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_kernel_name": (ctypes.c_char_p, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
@@ -147,6 +150,13 @@ def decode_workspace_bytes(B: int, H: int, H_kv: int, Tq: int, Tk: int, d: int) 
 
 def decode_splits(B: int, H_kv: int, Tk: int) -> int:
     return int(load_library().attn_decode_splits(B, H_kv, Tk))
+
+
+def attn_fwd_materialized(q, k, v, o, lse, s_buf, p_buf, B, H, T, d, causal, scale,
+                          stream=0) -> int:
+    """Raw materialised (three-kernel) forward: integer device addresses."""
+    return load_library().attn_fwd_materialized(q, k, v, o, lse, s_buf, p_buf, B, H, T, d,
+                                                int(causal), float(scale), stream or None)
 
 
 def flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
@@ -294,6 +304,39 @@ def decode(q, k_cache, v_cache, Tk: int | None = None, causal: bool = True,
         st = attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                          lse.data_ptr(), ws_ptr, ws_bytes, B, H, Hkv, Tq, Tk, Tcap, d, causal,
                          scale, s)
+    if st != 0:
+        raise AttnError(st, status_string(st))
+    return out, lse
+
+
+def forward_materialized(q, k, v, causal: bool = True, scale: float | None = None, out=None,
+                         lse=None, s_buf=None, p_buf=None, stream=None):
+    """The unfused three-kernel forward on bf16 tensors [B, H, T, d] (T a
+    multiple of 128): S (fp32) and P (bf16) go through device memory.
+    Returns (o, lse) like :func:`forward`."""
+    import torch
+
+    if q.dim() != 4 or not (q.shape == k.shape == v.shape):
+        raise ValueError("q, k, v must all have shape [B, H, T, d]")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+        raise ValueError("the materialised forward takes bfloat16 tensors")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous CUDA tensors")
+    B, H, T, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    if s_buf is None:
+        s_buf = torch.empty((B, H, T, T), dtype=torch.float32, device=q.device)
+    if p_buf is None:
+        p_buf = torch.empty((B, H, T, T), dtype=torch.bfloat16, device=q.device)
+    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
+    with torch.cuda.device(q.device):
+        st = attn_fwd_materialized(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), s_buf.data_ptr(), p_buf.data_ptr(), B, H, T,
+                                   d, causal, scale, s)
     if st != 0:
         raise AttnError(st, status_string(st))
     return out, lse

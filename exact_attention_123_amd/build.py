@@ -3,7 +3,8 @@
     python -m exact_attention_123_amd.build
 
 compiles ``csrc/attn_fwd.hip`` (forward), ``csrc/attn_bwd.hip`` (backward) and
-``csrc/attn_decode.hip`` (decode over a key/value cache) with hipcc into
+``csrc/attn_decode.hip`` (decode over a key/value cache) and
+``csrc/attn_materialized.hip`` (the unfused three-kernel forward) with hipcc into
 ``exact_attention_123_amd/libattn.so``.  The library exports the C ABI of
 ``include/attn.h``; the Python binding loads it with ctypes.
 """
@@ -16,7 +17,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip")]
+SRCS = [os.path.join(PKG, "csrc", n)
+        for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_materialized.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 

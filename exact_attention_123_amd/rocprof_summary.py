@@ -2,7 +2,9 @@
 ``profiles/``.
 
 A "pass" is the forward (one kernel per call, symbols containing
-``attn_fwd_``) or the backward (three kernels per call, ``attn_bwd_``).
+``attn_fwd_``), the backward (three kernels per call, ``attn_bwd_``) or the
+decode (one or two kernels per call, ``attn_decode_``) or the materialised
+forward (three kernels per call, ``attn_mat_``).
 Summaries per (name, workload), where name is the forward kernel's instance
 name or the backward's dK/dV kernel name:
 
@@ -46,9 +48,14 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
-SOURCES = {"fwd": os.path.join(PKG, "csrc", "attn_fwd.hip"),
-           "bwd": os.path.join(PKG, "csrc", "attn_bwd.hip")}
-MARKS = {"fwd": "attn_fwd_", "bwd": "attn_bwd_"}  # substring of the pass's symbols
+_CSRC = os.path.join(PKG, "csrc")
+# the kernel code of each pass: its source and the headers it includes
+SOURCES = {"fwd": [os.path.join(_CSRC, "attn_fwd.hip")],
+           "bwd": [os.path.join(_CSRC, "attn_bwd.hip"), os.path.join(_CSRC, "tiles.h")],
+           "decode": [os.path.join(_CSRC, "attn_decode.hip"), os.path.join(_CSRC, "tiles.h")],
+           "mat": [os.path.join(_CSRC, "attn_materialized.hip"), os.path.join(_CSRC, "tiles.h")]}
+# substring of the pass's kernel symbols
+MARKS = {"fwd": "attn_fwd_", "bwd": "attn_bwd_", "decode": "attn_decode_", "mat": "attn_mat_"}
 COPY_MARK = "copyBuffer"   # the runtime's device-to-device copy kernel
 
 
@@ -65,8 +72,11 @@ def code_sha(text: str) -> str:
 
 
 def source_sha(pass_: str = "fwd") -> str:
-    with open(SOURCES[pass_]) as f:
-        return code_sha(f.read())
+    text = ""
+    for path in SOURCES[pass_]:
+        with open(path) as f:
+            text += f.read() + "\n"
+    return code_sha(text)
 
 
 def _rows(path):

@@ -1,7 +1,8 @@
 /*
  * attn.h -- C ABI of the fused, I/O-aware forward pass of exact scaled
  * dot-product attention on AMD Instinct MI355X (gfx950), with its backward
- * pass, grouped-query variants of both, and decode over a key/value cache.
+ * pass, grouped-query variants of both, decode over a key/value cache, and
+ * the unfused (materialised) forward it is measured against.
  *
  * For every (batch b, head h) the library computes, for queries Q, keys K
  * and values V of shape T x d,
@@ -30,14 +31,14 @@
  * [B][H][T] float array.  All pointers are device pointers.
  *
  * Ownership.  The caller owns every buffer.  The library allocates, frees
- * and keeps no device memory; the forward uses no workspace, the backward and
- * the decode a caller-owned one (ws).  It holds no mutable state other than a per-device
+ * and keeps no device memory; the forward uses no workspace, the backward,
+ * the decode and the materialised forward caller-owned ones.  It holds no mutable state other than a per-device
  * cache of the architecture check, and may be called from several host
  * threads.
  *
  * Asynchrony.  Calls enqueue their kernels (one for the forward, three for
- * the backward, one or two for the decode) on `stream` (NULL = the null
- * stream) and return; they never synchronise.
+ * the backward and the materialised forward, one or two for the decode) on
+ * `stream` (NULL = the null stream) and return; they never synchronise.
  *
  * Errors.  Arguments are validated on the host before any HIP call; on a
  * validation error nothing is launched and the outputs are untouched.  An
@@ -205,6 +206,28 @@ int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv,
 /* Number of key ranges attn_decode splits each key/value head into
  * (0 if the sizes are invalid). */
 int64_t attn_decode_splits(int64_t B, int64_t H_kv, int64_t Tk);
+
+/*
+ * Materialised forward: the unfused three-kernel path that writes the T x T
+ * score matrix S (fp32) and probability matrix P (bf16) to device memory and
+ * reads them back ("Why Attention Is Difficult to Optimize", Figure 2: the
+ * naive sequence of separate kernels, each round-tripping through HBM), for
+ * measuring the time and traffic the fused forward avoids.  Same inputs,
+ * outputs and definitions as attn_fwd (O = P V with P rounded to bf16, LSE
+ * natural log).
+ *   s_buf: float [B][H][T][T] scratch, p_buf: __hip_bfloat16 [B][H][T][T]
+ *          scratch, both caller-owned and overwritten; under the causal mask
+ *          only the 64-key tiles at or below the diagonal of each 128-query
+ *          block are written and read;
+ *   T must be a multiple of 128 and at most 32768 (ATTN_ERR_UNSUPPORTED /
+ *          ATTN_ERR_SHAPE); d in {64, 128}.
+ * Three kernels are enqueued on `stream` (scores, row softmax, P V).
+ */
+attn_status attn_fwd_materialized(const void* q, const void* k, const void* v,
+                                  void* o, float* lse, float* s_buf,
+                                  void* p_buf, int64_t B, int64_t H, int64_t T,
+                                  int64_t d, int causal, float scale,
+                                  hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* attn_status_string(attn_status s);

@@ -218,3 +218,20 @@ def test_decode_split_sizes():
     assert ea.decode_splits(2048, 8, 4096) == 1
     assert ea.decode_workspace_bytes(2048, 32, 8, 1, 4096, 128) == 0
     assert ea.decode_workspace_bytes(1, 32, 8, 1, 131072, 128) == 128 * 32 * 129 * 4
+
+
+@no_gpu_only
+def test_materialized_validation_errors():
+    def mat(**kw):
+        a = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, s=1 << 36, p=2 << 36, B=1, H=1,
+                 T=256, d=64, causal=1, scale=0.1)
+        a.update(kw)
+        return ea.attn_fwd_materialized(a["q"], a["k"], a["v"], a["o"], a["lse"], a["s"],
+                                        a["p"], a["B"], a["H"], a["T"], a["d"], a["causal"],
+                                        a["scale"])
+    assert mat(T=200) == 3          # T must be a multiple of 128
+    assert mat(T=65536) == 2        # a head's scores must stay under 4 GiB
+    assert mat(d=96) == 3
+    assert mat(s=0) == 1
+    assert mat(p=A) == 6            # scratch overlaps q
+    assert mat(T=0) == 0
