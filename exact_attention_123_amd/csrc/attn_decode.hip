@@ -19,8 +19,11 @@
 //     group: the Tq G query rows (<= 32) form one MFMA column block;
 //   - the keys are split across workgroups (split-KV) so that the grid
 //     fills all 256 CUs, and inside a workgroup each wave streams its own
-//     32-key blocks (direct-to-LDS, two stages per wave, no workgroup
-//     barrier in the loop);
+//     32-key blocks, no workgroup barrier in the loop: K straight into
+//     registers (it is the A operand of the score MFMA as loaded), V
+//     direct-to-LDS (its transposing read needs LDS), both one block ahead.
+//     With only V in LDS (16 KiB per wave) two workgroups fit on a CU, so
+//     eight waves keep loads in flight;
 //   - partial results (running max, normalisers, output accumulator) of the
 //     4 waves merge in LDS with the rescaling of the online softmax; partial
 //     results of the splits merge in a second small kernel:
@@ -66,7 +69,7 @@ __device__ __forceinline__ float pair_max(float x) {
 // the split's normalised output and natural-log LSE per query row
 // (row index (bhq Tq + qi), NR rows), else unused and O, LSE written.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ part_o,
     float* __restrict__ part_lse, int Tq, int Tk, int Tcap, int G, int nsplit, int kps,
@@ -74,10 +77,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
   using C = RowTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
   constexpr int TB = kBlk * RB;  // bytes of one K or V block
-  // Two stages per wave for K and V, each stage its own object so that the
-  // compiler can tell the loads into one from the reads of the other.
-  __shared__ __attribute__((aligned(1024))) char sK0[kWaves][TB];
-  __shared__ __attribute__((aligned(1024))) char sK1[kWaves][TB];
+  // Two V stages per wave, each stage its own object so that the compiler
+  // can tell the loads into one from the reads of the other.
   __shared__ __attribute__((aligned(1024))) char sV0[kWaves][TB];
   __shared__ __attribute__((aligned(1024))) char sV1[kWaves][TB];
   __shared__ float sM[kWaves][kMaxRows], sL[kWaves][kMaxRows], sW[kWaves][kMaxRows];
@@ -93,12 +94,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
   const size_t qrow = ((size_t)bhkv * G + j / Tq) * Tq + qi;  // global query row
   const int pos = Tk - Tq + qi;                                // its position
 
-  // Q fragment: B operand [d][query] of S^T = K Q^T.
+  // Q fragment: B operand [d][query] of S^T = K Q^T.  The contraction
+  // over d takes k-step s of lane half h from d = 8 (NDS h + s) .. + 8, so
+  // that a lane's K operand over all steps is one contiguous run of its row.
   bf16x8_t qf[NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s) {
     qf[s] = bf16x8_t{};
-    if (row_ok) qf[s] = *reinterpret_cast<const bf16x8_t*>(Q + qrow * D + 16 * s + 8 * h);
+    if (row_ok)
+      qf[s] = *reinterpret_cast<const bf16x8_t*>(Q + qrow * D + 8 * (NDS * h + s));
   }
 
   const int k_lo = split * kps, k_hi = min(Tk, k_lo + kps);
@@ -111,12 +115,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
   ad.init(lane);
   TileDma<D, kBlk, 1> dma;
   dma.init(0, lane);
-  constexpr int PER = TileDma<D, kBlk, 1>::PER;  // load instructions per block and operand
-  // Keys >= k_hi read as zero (and are masked below).
-  auto load = [&](char* kt, char* vt, int i) __attribute__((always_inline)) {
+  constexpr int PER = TileDma<D, kBlk, 1>::PER;  // V load instructions per block
+  // K operand of lane (j, h): row row_perm(j) of the block, d from
+  // 8 NDS h on (see qf).  Keys >= k_hi read as zero (and are masked below).
+  const int krow = row_perm(j) * RB + 16 * NDS * h;
+  auto load = [&](bf16x8_t (&kr)[NDS], char* vt, int i) __attribute__((always_inline)) {
     const int kb0 = k_lo + kBlk * (wave + kWaves * i);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb0 * D, max(k_hi - kb0, 0) * RB);
     asm volatile("" ::: "memory");
-    dma.load(kt, Kh, k_hi, kb0, 0);
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      kr[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rk, krow + 16 * s));
     dma.load(vt, Vh, k_hi, kb0, 0);
   };
 
@@ -127,12 +136,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // One block: scores, mask, online softmax, O^T += V^T P^T.
-  auto block = [&](const char* kt, const char* vt, int i) __attribute__((always_inline)) {
+  auto block = [&](const bf16x8_t (&kr)[NDS], const char* vt, int i)
+      __attribute__((always_inline)) {
     const int kb0 = k_lo + kBlk * (wave + kWaves * i);
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int s = 0; s < NDS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(kt, ad.row[s]), qf[s], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], qf[s], sc, 0, 0, 0);
     // scores in log2 units (any sign of the scale); register 8 a + e holds
     // key kb0 + 16 a + 8 h + e of query row j
 #pragma unroll
@@ -196,36 +206,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_decode_kernel(
     asm volatile("" ::: "memory");
   };
   using Zero = std::integral_constant<int, 0>;
-  using Next = std::integral_constant<int, 2 * PER>;
+  using Next = std::integral_constant<int, NDS + PER>;  // one block's loads
 
-  if (nmine > 0) load(sK0[wave], sV0[wave], 0);
+  bf16x8_t k0[NDS], k1[NDS];
+  if (nmine > 0) load(k0, sV0[wave], 0);
   for (int i = 0; i < nmine; i += 2) {
     if (i + 1 < nmine) {
-      load(sK1[wave], sV1[wave], i + 1);
+      load(k1, sV1[wave], i + 1);
       wait_loads(Next{});
     } else {
       wait_loads(Zero{});
     }
-    block(sK0[wave], sV0[wave], i);
+    block(k0, sV0[wave], i);
     if (i + 1 >= nmine) break;
     if (i + 2 < nmine) {
-      load(sK0[wave], sV0[wave], i + 2);
+      load(k0, sV0[wave], i + 2);
       wait_loads(Next{});
     } else {
       wait_loads(Zero{});
     }
-    block(sK1[wave], sV1[wave], i + 1);
+    block(k1, sV1[wave], i + 1);
   }
 
   // Merge the four waves' partial results for each query row.
   l_run += __shfl_xor(l_run, 32);
   w_run += __shfl_xor(w_run, 32);
   __syncthreads();  // every wave is done with its LDS stages
-  // Wave w's 32 x D fp32 accumulator goes to half (w & 1) of sK0 (w < 2)
-  // or sK1 (w >= 2): each K stage holds exactly two of them.
-  static_assert(sizeof(sK0) == 2 * sizeof(float) * kMaxRows * D, "merge buffer");
+  // Wave w's 32 x D fp32 accumulator goes to half (w & 1) of sV0 (w < 2)
+  // or sV1 (w >= 2): each V stage holds exactly two of them.
+  static_assert(sizeof(sV0) == 2 * sizeof(float) * kMaxRows * D, "merge buffer");
   auto part = [&](int w) __attribute__((always_inline)) -> float* {
-    return reinterpret_cast<float*>(w < 2 ? &sK0[0][0] : &sK1[0][0]) + (w & 1) * kMaxRows * D;
+    return reinterpret_cast<float*>(w < 2 ? &sV0[0][0] : &sV1[0][0]) + (w & 1) * kMaxRows * D;
   };
   {
     float* mine = part(wave);
