@@ -135,6 +135,13 @@ __device__ __forceinline__ float pair_max(float x) {
 // 2^126 below the stale max flush to zero; relative to the true max they are
 // smaller still, so they are negligible either way.
 constexpr float kLazyRescale = 64.0f;
+// Bound on a lane's sum of one sub-tile's weights in the bf16 kernel (see
+// its softmax): above it the running max is raised.  kRegrow: the rows whose
+// sub-tile max outgrows the running max by more than this get a new one
+// (any row whose weights reached the bound did: its largest weight is then
+// above 2^60).
+constexpr float kMaxLaneSum = 18446744073709551616.0f;  // 2^64
+constexpr float kRegrow = 32.0f;
 
 // Online-softmax update for one wave's tile of scores ("FlashAttention --
 // avoid writing the giant intermediate", "Tiling and an incremental
@@ -447,51 +454,48 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
 
   // Online softmax of one 32-key score sub-tile x ("FlashAttention -- avoid
   // writing the giant intermediate", "Tiling and an incremental
-  // normalization"; "Attention Mechanism", section 3).  Produces the bf16
-  // weights pb, updates m_run, l_run, w_run and sets alpha to the factor the
-  // output accumulator must be multiplied by before pb is accumulated (1 for
-  // rows whose max did not move); returns whether any row of the wave has
-  // alpha != 1.
-  auto softmax = [&](f32x16_t& x, bf16x8_t(&pb)[2],
-                     float& alpha) __attribute__((always_inline)) -> bool {
-    // Row max over the sub-tile; the two lane halves holding a query's
-    // scores exchange theirs.
-    float mx = x[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-    const float mt = pair_max(mx) * cm;
-    // Raise a row's running max only when the sub-tile's max outgrows it by
-    // more than kLazyRescale (m = -inf on the first visible sub-tile always
-    // does).  The decision is per row, so a row's result never depends on
-    // other rows.
-    const bool grow = mt > m_run + kLazyRescale;
-    alpha = grow ? exp2_hw(m_run - mt) : 1.0f;
-    m_run = grow ? mt : m_run;
-    l_run *= alpha;
-    w_run *= alpha;
+  // normalization"; "Attention Mechanism", section 3), in two parts.
+  //
+  // softmax (every sub-tile, inside the MFMA block): the weights
+  // p = exp2(cm x - m) against the current running max m, their bf16
+  // rounding pb, the lane's partial sums ls (fp32) and ws (of the bf16
+  // weights), and whether any lane of the wave has ls above 2^64.  Below
+  // that bound every weight is at most 2^64 and m may stay where it is (the
+  // common factor cancels in acc / l): no row max is needed.
+  //
+  // regrow (only when some lane's sum passed the bound, including the first
+  // visible sub-tile, where m is still -1e38 and the weights are inf): the
+  // row max over the sub-tile (the two lane halves holding a query's scores
+  // exchange theirs) becomes the running max of the rows whose max outgrew
+  // m by more than kRegrow, the accumulator and normalisers of those rows
+  // are multiplied by exp2(m_old - m_new), and the weights are recomputed.
+  // The decision is per row, so a row's result never depends on other rows.
+  auto softmax = [&](const f32x16_t& x, bf16x8_t(&pb)[2], float& ls,
+                     float& ws) __attribute__((always_inline)) -> bool {
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(x[r], cm, -m_run));
-    l_run += sum_tree<16>(p);
+    ls = sum_tree<16>(p);
+    ws = 0.0f;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) pb[a][u] = (__bf16)p[8 * a + u];
-      // w_run sums exactly the bf16 weights the PV MFMA uses, so that O =
+      // ws sums exactly the bf16 weights the PV MFMA uses, so that O =
       // sum p'v / sum p' is a convex combination of V rows.
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 0, 1), one2,
-                                              w_run, false);
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 2, 3), one2,
-                                              w_run, false);
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 4, 5), one2,
-                                              w_run, false);
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 6, 7), one2,
-                                              w_run, false);
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 0, 1), one2, ws,
+                                           false);
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 2, 3), one2, ws,
+                                           false);
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 4, 5), one2, ws,
+                                           false);
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 6, 7), one2, ws,
+                                           false);
     }
     // Keep every softmax instruction in the MFMA block: without this the
-    // compiler may sink them past the rescale branch that follows.
-    asm volatile("" ::"v"(l_run), "v"(w_run), "v"(pb[0]), "v"(pb[1]));
-    return __builtin_amdgcn_ballot_w64(grow) != 0;
+    // compiler may sink them past the branch that follows.
+    asm volatile("" ::"v"(ls), "v"(ws), "v"(pb[0]), "v"(pb[1]));
+    return __builtin_amdgcn_ballot_w64(!(ls <= kMaxLaneSum)) != 0;
   };
 
   auto rescale = [&](float alpha) __attribute__((always_inline)) {
@@ -499,6 +503,33 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+  };
+
+  auto regrow = [&](const f32x16_t& x, bf16x8_t(&pb)[2], float& ls,
+                    float& ws) __attribute__((always_inline)) {
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+    const float mt = pair_max(mx) * cm;
+    const bool grow = mt > m_run + kRegrow;
+    const float alpha = grow ? exp2_hw(m_run - mt) : 1.0f;  // exp2(-huge) = 0
+    m_run = grow ? mt : m_run;
+    l_run *= alpha;
+    w_run *= alpha;
+    rescale(alpha);
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(x[r], cm, -m_run));
+    ls = sum_tree<16>(p);
+    ws = 0.0f;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        pb[a][u] = (__bf16)p[8 * a + u];
+        ws += (float)pb[a][u];
+      }
+    }
   };
 
   // Interleave the block's MFMAs with its LDS reads and VALU work; the LDS
@@ -542,10 +573,12 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
     if (k >= nfs) mask(scur, k);
     qk(kb, kh, snext);
     if constexpr (decltype(has_pv)::value) pv(vb, vh, pprev);
-    float alpha;
-    const bool any = softmax(scur, pcur, alpha);
+    float ls, ws;
+    const bool over = softmax(scur, pcur, ls, ws);
     interleave();
-    if (any) rescale(alpha);
+    if (over) regrow(scur, pcur, ls, ws);
+    l_run += ls;
+    w_run += ws;
   };
 
   // Iteration tau: sub-steps k = 2 tau + 1 and 2 tau + 2.  K_{tau+1} and V_tau
