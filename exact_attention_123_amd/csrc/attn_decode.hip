@@ -49,8 +49,12 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;            // keys per block (one MFMA score tile)
 constexpr int kMaxRows = 32;        // Tq * G query rows per key/value head
-constexpr int kMinSplitKeys = 256;  // smallest split: two blocks per wave
-constexpr int kTargetGroups = 1024; // workgroups the split aims for
+// Key split: about kTargetGroups workgroups (one round at two per CU), each
+// split at least kMinSplitKeys long: short splits cost a prologue, an LDS
+// merge and partial results each (measured: 32 splits of 4096 keys read a
+// 131072-key cache at 4.7 TB/s, 128 splits of 1024 keys at 3.3 TB/s).
+constexpr int kMinSplitKeys = 4096;
+constexpr int kTargetGroups = 512;
 // Running-max threshold (log2 units), as in the forward: the max is raised
 // only when a block's max exceeds it by more than this, so weights stay
 // below 2^64 and sums of at most 2^17 of them far inside fp32.
@@ -350,9 +354,10 @@ attn_status check_device() {
   return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
-// Split of the keys: enough workgroups to fill the chip (kTargetGroups over
-// B*H_kv groups), each split at least kMinSplitKeys keys and a multiple of
-// the 4 waves' 32-key blocks.  Returns nsplit and sets *kps.
+// Split of the keys: about kTargetGroups workgroups over the B*H_kv groups,
+// each split at least kMinSplitKeys keys (fewer splits when the cache is
+// short) and a multiple of the 4 waves' 32-key blocks.  Returns nsplit and
+// sets *kps.
 int64_t choose_split(int64_t BHkv, int64_t Tk, int64_t* kps) {
   int64_t want = (kTargetGroups + BHkv - 1) / BHkv;
   int64_t most = (Tk + kMinSplitKeys - 1) / kMinSplitKeys;

@@ -203,7 +203,7 @@ def test_decode_validation_errors():
     assert dec(o=A) == 6
     assert dec(Tq=0) == 0                  # nothing to do
     # the split needs a workspace here
-    assert ea.decode_workspace_bytes(1, 8, 2, 1, 100000, 128) > 0
+    assert ea.decode_workspace_bytes(1, 8, 2, 1, 100000, 128) > 0  # 25 splits
     far = dict(Tk=100000, Tcap=100000, q=1 << 36, k=2 << 36, v=3 << 36, o=4 << 36,
                lse=5 << 36)
     assert dec(ws=0, wsb=0, **far) == 9
@@ -211,13 +211,14 @@ def test_decode_validation_errors():
 
 
 def test_decode_split_sizes():
-    # enough splits to fill the chip, each at least 256 keys
-    assert ea.decode_splits(1, 8, 131072) == 128
-    assert ea.decode_splits(16, 8, 32768) == 8
+    # about 512 workgroups, each split at least 4096 keys
+    assert ea.decode_splits(1, 8, 131072) == 32
+    assert ea.decode_splits(16, 8, 32768) == 4
     assert ea.decode_splits(1, 1, 100) == 1
+    assert ea.decode_splits(1, 1, 40000) == 10
     assert ea.decode_splits(2048, 8, 4096) == 1
     assert ea.decode_workspace_bytes(2048, 32, 8, 1, 4096, 128) == 0
-    assert ea.decode_workspace_bytes(1, 32, 8, 1, 131072, 128) == 128 * 32 * 129 * 4
+    assert ea.decode_workspace_bytes(1, 32, 8, 1, 131072, 128) == 32 * 32 * 129 * 4
 
 
 @no_gpu_only

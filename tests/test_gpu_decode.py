@@ -89,7 +89,7 @@ def test_decode_many_splits():
     import exact_attention_123_amd as ea
     say("[decode splits] B=1 H=8 Hkv=1 Tq=2 Tk=40000")
     B, H, Hkv, Tq, Tk, d = 1, 8, 1, 2, 40000, 128
-    assert ea.decode_splits(B, Hkv, Tk) > 100
+    assert ea.decode_splits(B, Hkv, Tk) >= 8
     x = make_decode(B, H, Hkv, Tq, Tk, d, seed=9200, qk_mult=4.0)
     scale = 1.0 / math.sqrt(d)
     for causal in (True, False):
