@@ -92,10 +92,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
 
-  __shared__ __attribute__((aligned(1024))) char sQ[2][C::TBYTES];
-  __shared__ __attribute__((aligned(1024))) char sG[2][C::TBYTES];  // dO
-  __shared__ __attribute__((aligned(16))) float sL[2][kTile];       // LSE * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[2][kTile];       // Delta
+  // Two stages, each operand and stage its own object: the compiler then
+  // tells the direct-to-LDS loads into one stage from the reads of the
+  // other and does not wait for the loads in flight before reading.
+  __shared__ __attribute__((aligned(1024))) char sQ0[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char sQ1[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char sG0[C::TBYTES];  // dO
+  __shared__ __attribute__((aligned(1024))) char sG1[C::TBYTES];
+  __shared__ __attribute__((aligned(16))) float sL0[kTile];       // LSE * log2(e)
+  __shared__ __attribute__((aligned(16))) float sL1[kTile];
+  __shared__ __attribute__((aligned(16))) float sD0[kTile];       // Delta
+  __shared__ __attribute__((aligned(16))) float sD1[kTile];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,16 +135,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   // Query tile `qt` of member `m` of the group (query head bhkv G + m).
   // Row statistics: one dword per lane of wave 0 (L) and wave 1 (Delta),
   // lane L landing at 4 L; rows >= T read as zero.
-  auto stage = [&](int st, int m, int qt) __attribute__((always_inline)) {
+  auto stage = [&](char* tq, char* tg, float* tl, float* td, int m, int qt)
+      __attribute__((always_inline)) {
     const size_t bhq = (size_t)bhkv * G + m;
     const size_t qhead = bhq * (size_t)T * D;
     const int row0 = qt * kTile;
-    dma.load(sQ[st], Q + qhead, T, row0, wave);
-    dma.load(sG[st], dO + qhead, T, row0, wave);
+    dma.load(tq, Q + qhead, T, row0, wave);
+    dma.load(tg, dO + qhead, T, row0, wave);
     if (wave < 2) {
       const float* src = ws + (wave == 0 ? n : 0) + bhq * T + row0;
       const __amdgpu_buffer_rsrc_t r = make_rsrc(src, max(T - row0, 0) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(wave == 0 ? sL[st] : sD[st]), 4,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(wave == 0 ? tl : td), 4,
                                                lane * 4, 0, 0, 0);
     }
   };
@@ -155,15 +163,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   const int nqt = (T + kTile - 1) / kTile;
   const int per = nqt - qt0;  // > 0: k0 < T
   const int nit = G * per;
-  stage(0, 0, qt0);
-  __syncthreads();
-
-  for (int it = 0; it < nit; ++it) {
-    const int st = it & 1;
-    if (it + 1 < nit) stage(st ^ 1, (it + 1) / per, qt0 + (it + 1) % per);
+  // Query tile number `it` of the walk, staged in (tq, tg, tl, td).
+  auto tile = [&](const char* tq, const char* tg, const float* tl, const float* td, int it)
+      __attribute__((always_inline)) {
     const int qt = qt0 + it % per;
-    const char* tq = sQ[st];
-    const char* tg = sG[st];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i0 = qt * kTile + 32 * u;
@@ -184,10 +187,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int q8 = 32 * u + 16 * a + 8 * h;
-        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(&sL[st][q8]);
-        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&sL[st][q8 + 4]);
-        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&sD[st][q8]);
-        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&sD[st][q8 + 4]);
+        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(&tl[q8]);
+        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&tl[q8 + 4]);
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&td[q8]);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&td[q8 + 4]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float lse2 = e < 4 ? l0[e] : l1[e - 4];
@@ -213,10 +216,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
               lds_tr(tq, ro + ad.tr[0][dt], ro + ad.tr[1][dt]), db[a], dk[dt], 0, 0, 0);
         }
       }
+      // one sub-tile at a time: bounds the registers live at once
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // waits for the next stage's loads too (they have landed in LDS when
-    // the load counter drops) and frees this stage
+  };
+
+  stage(sQ0, sG0, sL0, sD0, 0, qt0);
+  __syncthreads();
+  // Two tiles per trip, alternating the stages: the loads of the next tile
+  // run while this one is computed; the barrier after each tile waits for
+  // them (and frees the stage just read).  No instruction is scheduled
+  // across the tiles (sched_barrier), which keeps the register pressure of
+  // one tile.
+  for (int it = 0; it < nit; it += 2) {
+    if (it + 1 < nit) stage(sQ1, sG1, sL1, sD1, (it + 1) / per, qt0 + (it + 1) % per);
+    tile(sQ0, sG0, sL0, sD0, it);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 >= nit) break;
+    if (it + 2 < nit) stage(sQ0, sG0, sL0, sD0, (it + 2) / per, qt0 + (it + 2) % per);
+    tile(sQ1, sG1, sL1, sD1, it + 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   store_rows<D>(dK + head, dk, scale, kw0 + j, T, h);
@@ -234,8 +255,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
 
-  __shared__ __attribute__((aligned(1024))) char sK[2][C::TBYTES];
-  __shared__ __attribute__((aligned(1024))) char sV[2][C::TBYTES];
+  // Two stages, each operand and stage its own object (see the dK/dV kernel).
+  __shared__ __attribute__((aligned(1024))) char sK0[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[C::TBYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[C::TBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -270,9 +294,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   ad.init(lane);
   TileDma<D, kTile, kWaves> dma;
   dma.init(wave, lane);
-  auto stage = [&](int st, int t) __attribute__((always_inline)) {
-    dma.load(sK[st], K + kvhead, T, t * kTile, wave);
-    dma.load(sV[st], V + kvhead, T, t * kTile, wave);
+  auto stage = [&](char* tk, char* tv, int t) __attribute__((always_inline)) {
+    dma.load(tk, K + kvhead, T, t * kTile, wave);
+    dma.load(tv, V + kvhead, T, t * kTile, wave);
   };
 
   f32x16_t dq[NDT];
@@ -281,14 +305,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(T, q0 + kBQ) : T;
   const int nkt = (kv_end + kTile - 1) / kTile;
-  if (nkt > 0) stage(0, 0);
-  __syncthreads();
-
-  for (int t = 0; t < nkt; ++t) {
-    const int st = t & 1;
-    if (t + 1 < nkt) stage(st ^ 1, t + 1);
-    const char* tk = sK[st];
-    const char* tv = sV[st];
+  // Key tile t, staged in (tk, tv).
+  auto tile = [&](const char* tk, const char* tv, int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kv0 = t * kTile + 32 * u;
@@ -326,8 +344,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
           dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               lds_tr(tk, ro + ad.tr[0][dt], ro + ad.tr[1][dt]), db[a], dq[dt], 0, 0, 0);
       }
+      // one sub-tile at a time: bounds the registers live at once
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if (nkt > 0) stage(sK0, sV0, 0);
+  __syncthreads();
+  // Two tiles per trip, alternating the stages (see the dK/dV kernel).
+  for (int t = 0; t < nkt; t += 2) {
+    if (t + 1 < nkt) stage(sK1, sV1, t + 1);
+    tile(sK0, sV0, t);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 >= nkt) break;
+    if (t + 2 < nkt) stage(sK0, sV0, t + 2);
+    tile(sK1, sV1, t + 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   store_rows<D>(dQ + head, dq, scale, qg, T, h);
