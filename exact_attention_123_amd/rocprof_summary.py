@@ -19,6 +19,12 @@ name or the backward's dK/dV kernel name:
     busy SIMD-cycles over (GPU-active cycles per XCD x 1024 SIMDs), and the
     clock that GPU-active cycles over the traced average duration imply.
 
+``<name>__<workload>__counters.md``
+    any other ``rocprofv3 --pmc`` passes (``--counters CSV --counters-cmd
+    CMD``, repeatable): each counter's value per call, summed over the
+    pass's kernels, and its share of ``SQ_WAVE_CYCLES`` when that counter
+    was collected in the same pass.
+
 ``<name>__<workload>__traffic.md``
     device-memory bytes per call from two ``rocprofv3 --pmc`` runs
     (``FETCH_SIZE``, then ``WRITE_SIZE``), each scaled by what the same
@@ -143,6 +149,9 @@ def main() -> int:
     ap.add_argument("--write-cmd", default="")
     ap.add_argument("--util", help="counter CSV of the MFMA utilisation pass")
     ap.add_argument("--util-cmd", default="")
+    ap.add_argument("--counters", action="append", default=[],
+                    help="counter CSV of another --pmc pass (repeatable)")
+    ap.add_argument("--counters-cmd", action="append", default=[])
     ap.add_argument("--out", default=PROFILES)
     a = ap.parse_args()
     os.makedirs(a.out, exist_ok=True)
@@ -185,6 +194,22 @@ def main() -> int:
                     + f"\nMFMA busy fraction: {util:.3f}\n\n"
                     f"non-MFMA VALU instructions per MFMA: {other:.2f}\n\n" + clock)
         print("wrote", base + "__mfma_util.md")
+
+    if a.counters:
+        parts = []
+        for i, path in enumerate(a.counters):
+            m, n = counters_mean(path, mark)
+            cmd = a.counters_cmd[i] if i < len(a.counters_cmd) else ""
+            wc = m.get("SQ_WAVE_CYCLES")
+            rows = "".join(
+                f"| {k} | {v:.6g} | " + (f"{v / wc:.3f}" if wc else "") + " |\n"
+                for k, v in sorted(m.items()))
+            parts.append(f"command: `{cmd}`\n\n| counter | per call ({n} calls) | "
+                         f"share of SQ_WAVE_CYCLES |\n|---|---|---|\n{rows}\n")
+        with open(base + "__counters.md", "w") as f:
+            f.write(f"# {a.name} on {a.workload}: SQ counters\n\n"
+                    f"kernel_code_sha256: {sha}\n\n" + "".join(parts))
+        print("wrote", base + "__counters.md")
 
     if a.fetch and a.write:
         copy_bytes = a.copy_mib * (1 << 20)
