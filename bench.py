@@ -237,7 +237,7 @@ def run_decode(args) -> int:
         "data": "synthetic: seeded PCG64 N(0,1) draws rounded to bf16 (RNE)",
         "config": {"workload": name, "pass": "decode", "B": B, "H": H, "H_kv": Hkv, "Tq": Tq,
                    "Tk": Tk, "d": d, "causal": causal, "scale": scale,
-                   "splits": ea.decode_splits(B, Hkv, Tk), "bytes_per_step": nbytes,
+                   "splits": ea.decode_splits(B, H, Hkv, Tq, Tk), "bytes_per_step": nbytes,
                    "kernel": kname, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

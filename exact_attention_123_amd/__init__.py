@@ -50,7 +50,7 @@ EXPORTS = {
     "attn_decode": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 8
                     + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_decode_workspace_bytes": (ctypes.c_int64, [ctypes.c_int64] * 6),
-    "attn_decode_splits": (ctypes.c_int64, [ctypes.c_int64] * 3),
+    "attn_decode_splits": (ctypes.c_int64, [ctypes.c_int64] * 5),
     "attn_fwd_materialized": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 4
                               + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -148,8 +148,8 @@ def decode_workspace_bytes(B: int, H: int, H_kv: int, Tq: int, Tk: int, d: int) 
     return int(load_library().attn_decode_workspace_bytes(B, H, H_kv, Tq, Tk, d))
 
 
-def decode_splits(B: int, H_kv: int, Tk: int) -> int:
-    return int(load_library().attn_decode_splits(B, H_kv, Tk))
+def decode_splits(B: int, H: int, H_kv: int, Tq: int, Tk: int) -> int:
+    return int(load_library().attn_decode_splits(B, H, H_kv, Tq, Tk))
 
 
 def attn_fwd_materialized(q, k, v, o, lse, s_buf, p_buf, B, H, T, d, causal, scale,

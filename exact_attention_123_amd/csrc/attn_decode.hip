@@ -16,7 +16,9 @@
 // its whole cache alone.  Here:
 //   - the G query heads that share a key/value head (grouped-query
 //     attention) are processed together, so the cache is read once per
-//     group: the Tq G query rows (<= 32) form one MFMA column block;
+//     group: the Tq G query rows form one MFMA column block (up to 32
+//     rows; more rows take one workgroup per 32-row chunk, which read the
+//     same keys from L2);
 //   - the keys are split across workgroups (split-KV) so that the grid
 //     fills all 256 CUs, and inside a workgroup each wave streams its own
 //     32-key blocks, no workgroup barrier in the loop: K straight into
@@ -48,7 +50,8 @@ using namespace attn_tiles;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;            // keys per block (one MFMA score tile)
-constexpr int kMaxRows = 32;        // Tq * G query rows per key/value head
+constexpr int kMaxRows = 32;        // query rows of one workgroup (one MFMA column block)
+constexpr int kMaxChunks = 8;       // Tq * G <= 256 query rows per key/value head
 // Key split: about kTargetGroups workgroups (one round at two per CU), each
 // split at least kMinSplitKeys long: short splits cost a prologue, an LDS
 // merge and partial results each (measured: 32 splits of 4096 keys read a
@@ -67,9 +70,10 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Workgroup (kv head bhkv, split s) over keys [s kps, min(Tk, (s + 1) kps)).
-// Query row j < R = Tq G of the group is member j / Tq (query head
-// bhkv G + j / Tq), new query j % Tq.  part_o / part_lse: when nsplit > 1,
+// Workgroup (row chunk, kv head bhkv, split s) over keys
+// [s kps, min(Tk, (s + 1) kps)).  Row r < R = Tq G of the group is member
+// r / Tq (query head bhkv G + r / Tq), new query r % Tq; the chunk holds rows
+// 32 chunk .. 32 chunk + 31.  part_o / part_lse: when nsplit > 1,
 // the split's normalised output and natural-log LSE per query row
 // (row index (bhq Tq + qi), NR rows), else unused and O, LSE written.
 template <int D, bool CAUSAL>
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ part_o,
     float* __restrict__ part_lse, int Tq, int Tk, int Tcap, int G, int nsplit, int kps,
-    int NR, float c) {
+    int NR, int nwg, float c) {
   using C = RowTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
   constexpr int TB = kBlk * RB;  // bytes of one K or V block
@@ -90,13 +94,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, h = lane >> 5;
+  // Workgroup id: row chunk outermost (nwg = B H_kv nsplit workgroups per
+  // chunk), so the chunks reading the same keys share an XCD when nwg is a
+  // multiple of 8.
   const int id = blockIdx.x;
-  const int bhkv = id / nsplit, split = id % nsplit;
-  const int R = Tq * G;
-  const bool row_ok = j < R;
-  const int qi = j % Tq;
-  const size_t qrow = ((size_t)bhkv * G + j / Tq) * Tq + qi;  // global query row
-  const int pos = Tk - Tq + qi;                                // its position
+  const int chunk = id / nwg, rest = id % nwg;
+  const int bhkv = rest / nsplit, split = rest % nsplit;
+  const int R = Tq * G;             // query rows of the group
+  const int r0 = kMaxRows * chunk;  // this workgroup's first row
+  const bool row_ok = r0 + j < R;
+  const int qi = (r0 + j) % Tq;
+  const size_t qrow = ((size_t)bhkv * G + (r0 + j) / Tq) * Tq + qi;  // global query row
+  const int pos = Tk - Tq + qi;                                      // its position
 
   // Q fragment: B operand [d][query] of S^T = K Q^T.  The contraction
   // over d takes k-step s of lane half h from d = 8 (NDS h + s) .. + 8, so
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
   // 8 threads per query row, D / 8 columns each.
   constexpr int CPT = D / 8;
   const int row = tid >> 3, c0 = (tid & 7) * CPT;
-  if (row >= R) return;
+  if (r0 + row >= R) return;
   float M = sM[0][row];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sM[w][row]);
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     o[u] = acc * inv;
   }
   const float lse = Lt > 0.0f ? (M + log2_hw(Lt)) * kLn2 : -INFINITY;
-  const size_t orow = ((size_t)bhkv * G + row / Tq) * Tq + row % Tq;
+  const size_t orow = ((size_t)bhkv * G + (r0 + row) / Tq) * Tq + (r0 + row) % Tq;
   if (nsplit == 1) {
 #pragma unroll
     for (int u = 0; u < CPT; u += 4) {
@@ -354,7 +363,11 @@ attn_status check_device() {
   return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
-// Split of the keys: about kTargetGroups workgroups over the B*H_kv groups,
+// Workgroups per (key/value head, split): one per 32 query rows.
+int64_t row_chunks(int64_t Tq, int64_t G) { return (Tq * G + kMaxRows - 1) / kMaxRows; }
+
+// Split of the keys: about kTargetGroups workgroups over the B*H_kv groups
+// (times their row chunks),
 // each split at least kMinSplitKeys keys (fewer splits when the cache is
 // short) and a multiple of the 4 waves' 32-key blocks.  Returns nsplit and
 // sets *kps.
@@ -387,12 +400,12 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
   // the new queries are the last Tq positions of the cache; a query needs at
   // least one key
   if (Tk < 1 || (causal && Tk < Tq)) return ATTN_ERR_SHAPE;
-  if (Tq * (H / H_kv) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  if (Tq * (H / H_kv) > kMaxRows * kMaxChunks) return ATTN_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if ((Tk_cap + 64) * d * 2 > kMaxHeadBytes) return ATTN_ERR_SHAPE;
   if (B > (int64_t(1) << 31) / H) return ATTN_ERR_SHAPE;
   if (B * H > (INT64_MAX / 8) / (Tk_cap * d * 2)) return ATTN_ERR_SHAPE;
-  if (B * H_kv * kTargetGroups > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (B * H_kv * kTargetGroups * kMaxChunks > INT32_MAX) return ATTN_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return ATTN_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return ATTN_ERR_ALIGN;
   const int64_t qb = B * H * Tq * d * 2, kb = B * H_kv * Tk_cap * d * 2, lb = B * H * Tq * 4;
@@ -416,8 +429,9 @@ extern "C" {
 int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
                                     int64_t d) {
   if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || (d != 64 && d != 128)) return 0;
+  if (H % H_kv != 0) return 0;
   int64_t kps;
-  const int64_t n = choose_split(B * H_kv, Tk, &kps);
+  const int64_t n = choose_split(B * H_kv * row_chunks(Tq, H / H_kv), Tk, &kps);
   return n > 1 ? n * B * H * Tq * (d + 1) * 4 : 0;
 }
 
@@ -430,7 +444,8 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
                             empty);
   if (st != ATTN_OK || empty) return st;
   int64_t kps;
-  const int64_t nsplit = choose_split(B * H_kv, Tk, &kps);
+  const int64_t nchunk = row_chunks(Tq, H / H_kv);
+  const int64_t nsplit = choose_split(B * H_kv * nchunk, Tk, &kps);
   const int64_t NR = B * H * Tq;
   const int64_t need = nsplit > 1 ? nsplit * NR * (d + 1) * 4 : 0;
   float* part_o = nullptr;
@@ -448,13 +463,13 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
   if ((st = check_device()) != ATTN_OK) return st;
 
   int tq = (int)Tq, tk = (int)Tk, tcap = (int)Tk_cap, g = (int)(H / H_kv), ns = (int)nsplit,
-      kp = (int)kps, nr = (int)NR;
+      kp = (int)kps, nr = (int)NR, nwg = (int)(B * H_kv * nsplit);
   float c = scale * kLog2e;
   void* args[] = {(void*)&q,  (void*)&k,  (void*)&v,    (void*)&o,  (void*)&lse,
                   (void*)&part_o, (void*)&part_lse, (void*)&tq, (void*)&tk, (void*)&tcap,
-                  (void*)&g,  (void*)&ns, (void*)&kp,   (void*)&nr, (void*)&c};
+                  (void*)&g,  (void*)&ns, (void*)&kp,   (void*)&nr, (void*)&nwg, (void*)&c};
   const void* kern = d == 64 ? decode_kernel<64>(causal) : decode_kernel<128>(causal);
-  const dim3 grid((unsigned)(B * H_kv * nsplit));
+  const dim3 grid((unsigned)(nwg * nchunk));
   if (hipLaunchKernel(kern, grid, dim3(kThreads), args, 0, stream) != hipSuccess)
     return ATTN_ERR_LAUNCH;
   if (nsplit > 1) {
@@ -470,10 +485,10 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
   return ATTN_OK;
 }
 
-int64_t attn_decode_splits(int64_t B, int64_t H_kv, int64_t Tk) {
-  if (B <= 0 || H_kv <= 0 || Tk <= 0) return 0;
+int64_t attn_decode_splits(int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || H % H_kv != 0) return 0;
   int64_t kps;
-  return choose_split(B * H_kv, Tk, &kps);
+  return choose_split(B * H_kv * row_chunks(Tq, H / H_kv), Tk, &kps);
 }
 
 }  // extern "C"

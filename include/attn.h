@@ -177,14 +177,16 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
  *   k, v:  const __hip_bfloat16 caches [B][H_kv][Tk_cap][d] of which rows
  *          0 .. Tk-1 of each head are valid (rows >= Tk are never read);
  *   H_kv divides H, query head h reads key/value head h / (H / H_kv);
- *   Tq * (H / H_kv) <= 32 (more new queries per key/value head are a
- *          prefill: ATTN_ERR_UNSUPPORTED);  1 <= Tk <= Tk_cap, and Tk >= Tq
- *          when causal (ATTN_ERR_SHAPE otherwise);
+ *   Tq * (H / H_kv) <= 256 (more new queries per key/value head are a
+ *          prefill: ATTN_ERR_UNSUPPORTED); up to 32 of them share one
+ *          workgroup and one read of the keys, more take one workgroup per
+ *          32 rows;  1 <= Tk <= Tk_cap, and Tk >= Tq when causal
+ *          (ATTN_ERR_SHAPE otherwise);
  *   ws, ws_bytes: caller-owned device workspace of at least
  *          attn_decode_workspace_bytes(B, H, H_kv, Tq, Tk, d) bytes,
  *          16-byte aligned (may be NULL when that is 0), overwritten.  Too
  *          small: ATTN_ERR_WORKSPACE.
- * The keys are split into attn_decode_splits(B, H_kv, Tk) consecutive
+ * The keys are split into attn_decode_splits(B, H, H_kv, Tq, Tk) consecutive
  * ranges, one workgroup each, whose partial results (normalised output and
  * LSE per query row, fp32, in ws) a second kernel merges as
  * LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.  The query heads
@@ -205,7 +207,8 @@ int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv,
 
 /* Number of key ranges attn_decode splits each key/value head into
  * (0 if the sizes are invalid). */
-int64_t attn_decode_splits(int64_t B, int64_t H_kv, int64_t Tk);
+int64_t attn_decode_splits(int64_t B, int64_t H, int64_t H_kv, int64_t Tq,
+                           int64_t Tk);
 
 /*
  * Materialised forward: the unfused three-kernel path that writes the T x T

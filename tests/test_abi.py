@@ -196,7 +196,7 @@ def test_decode_validation_errors():
     assert dec(Tk=0) == 2                  # a query needs a key
     assert dec(Tq=3, Tk=2, Tcap=2) == 2    # causal: the queries are cache positions
     assert dec(Tcap=50) == 2               # valid length beyond capacity
-    assert dec(Tq=9) == 3                  # 9 * 4 rows > 32 per key/value head
+    assert dec(Tq=65) == 3                 # 65 * 4 rows > 256 per key/value head
     assert dec(d=96) == 3
     assert dec(q=0) == 1
     assert dec(causal=2) == 6
@@ -212,11 +212,14 @@ def test_decode_validation_errors():
 
 def test_decode_split_sizes():
     # about 512 workgroups, each split at least 4096 keys
-    assert ea.decode_splits(1, 8, 131072) == 32
-    assert ea.decode_splits(16, 8, 32768) == 4
-    assert ea.decode_splits(1, 1, 100) == 1
-    assert ea.decode_splits(1, 1, 40000) == 10
-    assert ea.decode_splits(2048, 8, 4096) == 1
+    assert ea.decode_splits(1, 32, 8, 1, 131072) == 32
+    assert ea.decode_splits(16, 32, 8, 1, 32768) == 4
+    assert ea.decode_splits(1, 1, 1, 1, 100) == 1
+    assert ea.decode_splits(1, 8, 1, 2, 40000) == 10
+    assert ea.decode_splits(2048, 32, 8, 1, 4096) == 1
+    # 64 query rows per key/value head: two row chunks, half the splits
+    assert ea.decode_splits(1, 32, 8, 1, 262144) == 64
+    assert ea.decode_splits(1, 32, 8, 16, 262144) == 32
     assert ea.decode_workspace_bytes(2048, 32, 8, 1, 4096, 128) == 0
     assert ea.decode_workspace_bytes(1, 32, 8, 1, 131072, 128) == 32 * 32 * 129 * 4
 

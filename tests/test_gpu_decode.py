@@ -57,7 +57,7 @@ def check(x, O, L, causal, scale, Tk, heads=None):
 
 CASES = []
 for Tq, H, Hkv in ((1, 8, 8), (1, 32, 8), (1, 8, 1), (2, 8, 2), (4, 8, 8), (4, 16, 2),
-                   (32, 4, 4)):
+                   (32, 4, 4), (8, 32, 4), (5, 16, 1), (64, 2, 2)):
     for Tk in (1, 7, 33, 100, 1000, 5000):
         if Tk >= Tq:
             CASES.append((Tq, H, Hkv, Tk))
@@ -89,7 +89,7 @@ def test_decode_many_splits():
     import exact_attention_123_amd as ea
     say("[decode splits] B=1 H=8 Hkv=1 Tq=2 Tk=40000")
     B, H, Hkv, Tq, Tk, d = 1, 8, 1, 2, 40000, 128
-    assert ea.decode_splits(B, Hkv, Tk) >= 8
+    assert ea.decode_splits(B, H, Hkv, Tq, Tk) >= 8
     x = make_decode(B, H, Hkv, Tq, Tk, d, seed=9200, qk_mult=4.0)
     scale = 1.0 / math.sqrt(d)
     for causal in (True, False):
