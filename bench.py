@@ -389,6 +389,9 @@ def main() -> int:
     ap.add_argument("--pass", dest="pass_", choices=["fwd", "bwd", "decode", "mat"],
                     default="fwd")
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--mask", choices=["causal", "full"], default=None,
+                    help="forward/backward: which of the workload's masks to run "
+                         "(default: its first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=None,
                     help="heads (fwd, bwd) or sequences (decode) of the workload the CPU "
@@ -419,6 +422,11 @@ def main() -> int:
 
     w = WORKLOADS[args.workload]
     causal = w["causal"][0]
+    if args.mask is not None:
+        causal = args.mask == "causal"
+        if causal not in w["causal"]:
+            print(f"workload {args.workload} has no {args.mask} mask", file=sys.stderr)
+            return 2
     B, H, T, d, dt = w["B"], w["H"], w["T"], w["d"], w["dtype"]
     bwd = args.pass_ == "bwd"
     Hkv = w.get("H_kv", H)
@@ -519,7 +527,9 @@ def main() -> int:
     peak = PEAK_TFLOPS[dt]
     traffic = measured_traffic(kname, args.workload, args.pass_)
 
-    config = {"workload": args.workload, "pass": args.pass_, "B": B, "H": H, "H_kv": Hkv,
+    config = {"workload": args.workload + (("_causal" if causal else "_full")
+                                           if len(w["causal"]) > 1 else ""),
+              "pass": args.pass_, "B": B, "H": H, "H_kv": Hkv,
               "T": T, "d": d,
               "causal": causal, "scale": scale, "qk_mult": w.get("qk_mult", 1.0),
               "flops_per_step": fl, "kernel": kname, "parallelism": "single GPU"}

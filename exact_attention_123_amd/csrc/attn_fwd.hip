@@ -298,7 +298,16 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
   const __bf16* Kh = K + kvhead;
   const __bf16* Vh = V + kvhead;
   const int q0 = qb * kBRBf16;
-  const int qg = q0 + wave * 32 + j;
+  // Row group of the wave: waves w and w + 4 share a SIMD, and under a
+  // causal mask a row group's work in the block's last (diagonal) tiles
+  // grows with its index, so the pair takes groups w and 7 - w.
+  const int rg = wave < 4 ? wave : 11 - wave;
+  const int qg = q0 + rg * 32 + j;
+  // Under a causal mask the last score sub-tile (32 keys) with a key visible
+  // to some row of the wave is klast = q0 / 32 + rg; from iteration tskip on
+  // (sub-steps k >= 2 tskip + 1 > klast + 1: nothing left to accumulate)
+  // the wave only loads its share of the tiles and joins the barriers.
+  const int tskip = CAUSAL ? (q0 / 32 + rg) / 2 + 1 : INT32_MAX;
 
   // Q fragment: B operand of S^T = K Q^T; lane (j, h) holds
   // Q[qg][16 s + 8 h .. +8] for every k-step s.  Rows >= T read as zero.
@@ -593,8 +602,10 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
     char* vfree = R == 0 ? sV2 : R == 1 ? sV0 : sV1;
     dma_k(kfree, tau + 3);
     dma_v(vfree, tau + 2);
-    substep(std::true_type{}, kcur, 0, vcur, 0, sY, sX, pX, pY, 2 * tau + 1);
-    substep(std::true_type{}, kcur, 1, vcur, 1, sX, sY, pY, pX, 2 * tau + 2);
+    if (tau < tskip) {
+      substep(std::true_type{}, kcur, 0, vcur, 0, sY, sX, pX, pY, 2 * tau + 1);
+      substep(std::true_type{}, kcur, 1, vcur, 1, sX, sY, pY, pX, 2 * tau + 2);
+    }
     // Every wave issued KPER + VPER loads this iteration: waiting down to
     // that many in flight means K_{tau+2} and V_{tau+1} have landed.
     wait_dma(std::integral_constant<int, KPER + VPER>{});
