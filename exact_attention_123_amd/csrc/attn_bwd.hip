@@ -170,8 +170,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i0 = qt * kTile + 32 * u;
-      // every query of the sub-tile precedes every key of the wave
-      if (CAUSAL && i0 + 31 < kw0) continue;
+      // Nothing to add when every query of the sub-tile precedes every key
+      // of the wave (causal) or lies past the end of the sequence (its Q
+      // and dO rows read as zero).  Without a branch here the non-causal
+      // kernels need up to 512 registers per lane and spill.
+      if (CAUSAL ? i0 + 31 < kw0 : i0 >= T) continue;
       f32x16_t S = f32x16_t{}, dP = f32x16_t{};
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
