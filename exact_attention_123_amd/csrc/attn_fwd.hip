@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "tiles.h"
 
 namespace {
 
@@ -203,14 +204,13 @@ struct Bf16Tile {
   static constexpr int NDT = D / 32;        // 32-row d tiles of O^T
   static constexpr int RB = D * 2;          // bytes per row of Q, K, V, O
   static constexpr int NCH = D / 8;         // 16-byte chunks per row
-  // K tile in LDS: each row is followed by one unused 16-byte slot, so rows
-  // sit NCH + 1 (an odd number of) slots apart and the 16 rows that one
-  // 16-lane phase of a 128-bit LDS read touches fall in 16 different banks.
-  static constexpr int KSLOT = NCH + 1;
-  static constexpr int KROWB = KSLOT * 16;
-  static constexpr int KBYTES = BC * KROWB;
-  static constexpr int KDMA = KBYTES / 1024;       // 1 KiB direct-to-LDS blocks
-  static constexpr int KPER = (KDMA + NW - 1) / NW;  // load instructions per wave
+  // K tile in LDS: unpadded rows, the 16-byte chunk c of row r at chunk
+  // c ^ attn_tiles::swz<D>(r), which is one-to-one on 16 consecutive rows:
+  // the 16 rows that one 16-lane phase of a 128-bit LDS read touches (one
+  // chunk each) fall in 16 different bank groups.
+  static constexpr int KBYTES = BC * RB;
+  static constexpr int KDMA = KBYTES / 1024;  // 1 KiB direct-to-LDS blocks
+  static constexpr int KPER = KDMA / NW;      // load instructions per wave
   // V tile in LDS: unpadded rows with an XOR swizzle of the 16-byte chunks
   // (see v_chunk_swizzle), 1 KiB blocks of RPK rows.
   static constexpr int VBYTES = BC * RB;
@@ -218,7 +218,7 @@ struct Bf16Tile {
   static constexpr int VPER = VDMA / NW;
   static constexpr int RPK = 1024 / RB;
   static constexpr int RPB = 256 / RB;      // rows per 256-byte bank cycle
-  static_assert(KBYTES % 1024 == 0 && VDMA % NW == 0 && VPER <= 4, "tile split");
+  static_assert(KDMA % NW == 0 && VDMA % NW == 0 && VPER <= 4, "tile split");
   static_assert(NST * (KBYTES + VBYTES) <= 160 * 1024, "LDS");
 };
 
@@ -269,8 +269,8 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, int G, float c) {
   using C = Bf16Tile<D>;
   constexpr int NW = C::NW, BC = C::BC, NDS = C::NDS, NDT = C::NDT;
-  constexpr int RB = C::RB, NCH = C::NCH, KSLOT = C::KSLOT, KROWB = C::KROWB;
-  constexpr int KDMA = C::KDMA, KPER = C::KPER, VPER = C::VPER, RPK = C::RPK;
+  constexpr int RB = C::RB, NCH = C::NCH;
+  constexpr int KPER = C::KPER, VPER = C::VPER, RPK = C::RPK;
   static_assert(BC == 64, "two 32-key score sub-tiles per LDS tile");
 
   // LDS: three K and three V stages, separate objects so that the compiler
@@ -281,10 +281,6 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
   __shared__ __attribute__((aligned(1024))) char sV2[C::VBYTES];
-  // Target of the K load instructions of waves that have no K block left
-  // (KDMA is not a multiple of NW): every wave then issues the same number
-  // of loads per tile, which keeps the wait counts below exact.  Never read.
-  __shared__ __attribute__((aligned(1024))) char sSink[1024];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,15 +324,14 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
 
   // Direct-to-LDS loads.  A 1 KiB block is written by one wave instruction,
   // lane L's 16 bytes landing at block offset 16 L; each lane picks the
-  // global chunk that belongs there.  K: block b holds padded slots
-  // 64 b .. 64 b + 63 (slot u = row u / KSLOT, chunk u % KSLOT; the pad slot
-  // re-reads the row's last chunk).  Wave w writes blocks w, w + NW, ...
+  // global chunk that belongs there.  K: block b holds rows RPK b ..
+  // RPK b + RPK - 1, swizzled; wave w writes blocks w, w + NW, ...
   int koff[KPER];
 #pragma unroll
   for (int n = 0; n < KPER; ++n) {
-    const int u = 64 * (wave + NW * n) + lane;
-    const int r = u / KSLOT, ch = u % KSLOT;
-    koff[n] = r * RB + 16 * (ch < NCH ? ch : NCH - 1);
+    const int r = RPK * (wave + NW * n) + lane / NCH;
+    const int pc = lane % NCH;
+    koff[n] = r * RB + 16 * (pc ^ attn_tiles::swz<D>(r));
   }
   // V: wave w writes blocks VPER w .. VPER w + VPER - 1 (block b holds rows
   // RPK b .. RPK b + RPK - 1).
@@ -352,16 +347,13 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
   auto dma_k = [&](char* buf, int t) __attribute__((always_inline)) {
     const int kv0 = t * BC;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Kh + (size_t)kv0 * D, max(kv_bytes - kv0 * RB, 0));
-    const __amdgpu_buffer_rsrc_t none = make_rsrc(Kh, 0);
 #pragma unroll
     for (int n = 0; n < KPER; ++n) {
       // (a plain local: host-side template instantiation drops the kernel
       // when an array element is passed to this builtin directly)
       const int off = koff[n];
-      const bool real = wave + NW * n < KDMA;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          real ? r : none, (lds_void_t*)(real ? buf + 1024 * (wave + NW * n) : sSink), 16, off,
-          0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(buf + 1024 * (wave + NW * n)), 16,
+                                               off, 0, 0, 0);
     }
   };
   auto dma_v = [&](char* buf, int t) __attribute__((always_inline)) {
@@ -400,8 +392,15 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
   };
 
   // LDS read addresses.  K (A operand of the QK MFMA): lane (j, h) reads row
-  // 32 half + perm(j), chunk 2 s + h.
-  const int kaddr = key_row_perm(j) * KROWB + 16 * h;
+  // 32 half + perm(j), chunk 2 s + h (stored at chunk (2 s + h) ^ swz; the
+  // swizzle has period 16 in the row, so the half adds a plain offset).
+  int kaddr[NDS];
+  {
+    const int r = key_row_perm(j);
+    const int f = attn_tiles::swz<D>(r);
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) kaddr[s] = r * RB + 16 * ((2 * s + h) ^ f);
+  }
   // V (A operand of the PV MFMA, V^T): ds_read_b64_tr_b16 gives lane i of a
   // 16-lane group element (i % 4) of the 8 bytes read by lane 4 e + i / 4 of
   // the group, in slot e.  Lane l of group g reads V[row][d .. d + 3] with
@@ -435,11 +434,10 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
   // S^T of the 32-key half `half` of the K tile in `kb`.
   auto qk = [&](const char* kb, int half, f32x16_t& sn) __attribute__((always_inline)) {
     sn = f32x16_t{};
-    const char* base = kb + kaddr;
+    const char* base = kb + half * 32 * RB;
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
-      const bf16x8_t a =
-          *reinterpret_cast<const bf16x8_t*>(base + half * 32 * KROWB + 32 * s);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(base + kaddr[s]);
       sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sn, 0, 0, 0);
     }
   };
