@@ -512,18 +512,25 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
   };
 
-  auto regrow = [&](const f32x16_t& x, bf16x8_t(&pb)[2], float& ls,
+  // first: the workgroup's first sub-tile, where nothing has been
+  // accumulated yet: the row max becomes the running max directly (it stays
+  // -1e38 for a row whose scores are all masked) and nothing is rescaled.
+  auto regrow = [&](auto first, const f32x16_t& x, bf16x8_t(&pb)[2], float& ls,
                     float& ws) __attribute__((always_inline)) {
     float mx = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
     const float mt = pair_max(mx) * cm;
-    const bool grow = mt > m_run + kRegrow;
-    const float alpha = grow ? exp2_hw(m_run - mt) : 1.0f;  // exp2(-huge) = 0
-    m_run = grow ? mt : m_run;
-    l_run *= alpha;
-    w_run *= alpha;
-    rescale(alpha);
+    if constexpr (decltype(first)::value) {
+      m_run = mt > m_run ? mt : m_run;
+    } else {
+      const bool grow = mt > m_run + kRegrow;
+      const float alpha = grow ? exp2_hw(m_run - mt) : 1.0f;  // exp2(-huge) = 0
+      m_run = grow ? mt : m_run;
+      l_run *= alpha;
+      w_run *= alpha;
+      rescale(alpha);
+    }
     float p[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(x[r], cm, -m_run));
@@ -579,11 +586,16 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
     }
     if (k >= nfs) mask(scur, k);
     qk(kb, kh, snext);
-    if constexpr (decltype(has_pv)::value) pv(vb, vh, pprev);
     float ls, ws;
-    const bool over = softmax(scur, pcur, ls, ws);
-    interleave();
-    if (over) regrow(scur, pcur, ls, ws);
+    if constexpr (decltype(has_pv)::value) {
+      pv(vb, vh, pprev);
+      const bool over = softmax(scur, pcur, ls, ws);
+      interleave();
+      if (over) regrow(std::false_type{}, scur, pcur, ls, ws);
+    } else {
+      // the first sub-tile (no P V yet): straight to the row max
+      regrow(std::true_type{}, scur, pcur, ls, ws);
+    }
     l_run += ls;
     w_run += ws;
   };
