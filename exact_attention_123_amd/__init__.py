@@ -22,7 +22,7 @@ __all__ = [
     "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_fwd_gqa",
     "attn_bwd_gqa", "attn_decode", "decode", "decode_workspace_bytes", "decode_splits",
     "attn_fwd_materialized", "forward_materialized",
-    "kernel_name",
+    "kernel_name", "fwd_kernel_name_for",
     "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
     "LIB_PATH", "STATUS", "flops", "bwd_flops",
 ]
@@ -55,6 +55,7 @@ EXPORTS = {
                               + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_kernel_name": (ctypes.c_char_p, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
+    "attn_fwd_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
 }
 
@@ -95,6 +96,13 @@ def status_string(code: int) -> str:
 
 def kernel_name(is_f32: bool, d: int, causal: bool):
     n = load_library().attn_kernel_name(int(bool(is_f32)), int(d), int(bool(causal)))
+    return None if n is None else n.decode()
+
+
+def fwd_kernel_name_for(B: int, H: int, T: int, d: int, causal: bool):
+    """The bf16 forward instance attn_fwd launches for these sizes on the
+    current device (needs a GPU)."""
+    n = load_library().attn_fwd_kernel_name_for(B, H, T, d, int(bool(causal)))
     return None if n is None else n.decode()
 
 

@@ -60,9 +60,9 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 // fp32 kernel: 4 waves, 128 query rows per workgroup (32 per wave).
 constexpr int kThreads = 256;
 constexpr int kBR = 128;
-// bf16 kernel: 8 waves, 256 query rows per workgroup (32 per wave).
-constexpr int kThreadsBf16 = 512;
-constexpr int kBRBf16 = 256;
+// bf16 kernel: 8 waves, 256 query rows per workgroup (32 per wave), or 4
+// waves and 128 rows when the 8-wave grid has fewer workgroups than the GPU
+// has CUs (see pick_waves).
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -195,9 +195,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-template <int D>
+template <int D, int NW_ = 8>
 struct Bf16Tile {
-  static constexpr int NW = kThreadsBf16 / 64;  // waves per workgroup
+  static constexpr int NW = NW_;            // waves per workgroup
   static constexpr int BC = 64;             // keys per tile
   static constexpr int NST = 3;             // LDS stages per operand
   static constexpr int NDS = D / 16;        // 16-wide d steps of the QK MFMA
@@ -263,11 +263,12 @@ __device__ __forceinline__ float sum_tree(const float* x) {
 // PRESCALE: multiply the scores by c before the softmax (any sign of c);
 // otherwise (c > 0) the multiply is folded into the exponent's fma and the
 // max is taken over the raw scores.
-template <int D, bool CAUSAL, bool PRESCALE>
-__global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
+template <int D, bool CAUSAL, bool PRESCALE, int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, int G, float c) {
-  using C = Bf16Tile<D>;
+  using C = Bf16Tile<D, NWAVES>;
+  constexpr int BR = 32 * NWAVES;  // query rows per workgroup
   constexpr int NW = C::NW, BC = C::BC, NDS = C::NDS, NDT = C::NDT;
   constexpr int RB = C::RB, NCH = C::NCH;
   constexpr int KPER = C::KPER, VPER = C::VPER, RPK = C::RPK;
@@ -293,11 +294,12 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
   const int head_bytes = T * RB;
   const __bf16* Kh = K + kvhead;
   const __bf16* Vh = V + kvhead;
-  const int q0 = qb * kBRBf16;
-  // Row group of the wave: waves w and w + 4 share a SIMD, and under a
-  // causal mask a row group's work in the block's last (diagonal) tiles
-  // grows with its index, so the pair takes groups w and 7 - w.
-  const int rg = wave < 4 ? wave : 11 - wave;
+  const int q0 = qb * BR;
+  // Row group of the wave: with 8 waves, waves w and w + 4 share a SIMD,
+  // and under a causal mask a row group's work in the block's last
+  // (diagonal) tiles grows with its index, so the pair takes groups w and
+  // 7 - w.
+  const int rg = NW == 8 && wave >= 4 ? 11 - wave : wave;
   const int qg = q0 + rg * 32 + j;
   // Under a causal mask the last score sub-tile (32 keys) with a key visible
   // to some row of the wave is klast = q0 / 32 + rg; from iteration tskip on
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(kThreadsBf16, 1) void attn_fwd_bf16_kernel(
       qf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rQ, qg * RB + (16 * s + 8 * h) * 2));
   }
 
-  const int kv_end = CAUSAL ? min(T, q0 + kBRBf16) : T;
+  const int kv_end = CAUSAL ? min(T, q0 + BR) : T;
   const int ntiles = (kv_end + BC - 1) / BC;
   const int kv_bytes = kv_end * RB;
   // Score sub-tiles (32 keys) below nfs need no mask: every key is < T and,
@@ -856,8 +858,10 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
   return ATTN_OK;
 }
 
-// Per-device cache of "is this a gfx950": 0 unknown, 1 yes, 2 no.
+// Per-device cache of "is this a gfx950" (0 unknown, 1 yes, 2 no) and of
+// its compute-unit count.
 std::atomic<int> g_arch_ok[64];
+std::atomic<int> g_cus[64];
 
 attn_status check_device() {
   int dev = 0;
@@ -868,9 +872,26 @@ attn_status check_device() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
     s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     g_arch_ok[dev].store(s, std::memory_order_relaxed);
   }
   return s == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+// Waves per workgroup of the bf16 kernel for these sizes on the current
+// device (after check_device): 8 (256 query rows) unless that grid has
+// fewer workgroups than the device has CUs; then 4 (128 rows), which
+// doubles the workgroups and halves each one's time per key tile (one wave
+// per SIMD instead of two): small problems are bound by the latency of
+// their longest query block.
+int pick_waves(int64_t B, int64_t H, int64_t T) {
+  int dev = 0;
+  int cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    const int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) cus = n;
+  }
+  return B * H * ((T + 255) / 256) < cus ? 4 : 8;
 }
 
 // Launches one workgroup of `threads` threads per `rows` query rows of each
@@ -888,16 +909,18 @@ attn_status launch(const void* kernel, int threads, int rows, const Elem* q, con
   return ATTN_OK;
 }
 
-template <bool PRESCALE>
+template <bool PRESCALE, int NW>
 const void* bf16_kernel_p(int64_t d, int causal) {
-  if (d == 64) return causal ? (const void*)attn_fwd_bf16_kernel<64, true, PRESCALE>
-                             : (const void*)attn_fwd_bf16_kernel<64, false, PRESCALE>;
-  return causal ? (const void*)attn_fwd_bf16_kernel<128, true, PRESCALE>
-                : (const void*)attn_fwd_bf16_kernel<128, false, PRESCALE>;
+  if (d == 64) return causal ? (const void*)attn_fwd_bf16_kernel<64, true, PRESCALE, NW>
+                             : (const void*)attn_fwd_bf16_kernel<64, false, PRESCALE, NW>;
+  return causal ? (const void*)attn_fwd_bf16_kernel<128, true, PRESCALE, NW>
+                : (const void*)attn_fwd_bf16_kernel<128, false, PRESCALE, NW>;
 }
 
-const void* bf16_kernel(int64_t d, int causal, float scale) {
-  return scale > 0.0f ? bf16_kernel_p<false>(d, causal) : bf16_kernel_p<true>(d, causal);
+const void* bf16_kernel(int64_t d, int causal, float scale, int nw) {
+  if (nw == 4)
+    return scale > 0.0f ? bf16_kernel_p<false, 4>(d, causal) : bf16_kernel_p<true, 4>(d, causal);
+  return scale > 0.0f ? bf16_kernel_p<false, 8>(d, causal) : bf16_kernel_p<true, 8>(d, causal);
 }
 
 const void* f32_kernel(int64_t d, int causal) {
@@ -918,7 +941,8 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   attn_status st = validate(q, k, v, o, lse, B, H, H_kv, T, d, causal, scale, 2, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  return launch<__bf16>(bf16_kernel(d, causal, scale), kThreadsBf16, kBRBf16, (const __bf16*)q,
+  const int nw = pick_waves(B, H, T);
+  return launch<__bf16>(bf16_kernel(d, causal, scale, nw), 64 * nw, 32 * nw, (const __bf16*)q,
                         (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, B, H, H_kv, T,
                         scale, stream);
 }
@@ -954,6 +978,18 @@ const char* attn_status_string(attn_status s) {
     case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than required";
   }
   return "unknown status";
+}
+
+const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d, int causal) {
+  if (B <= 0 || H <= 0 || T <= 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1))
+    return nullptr;
+  if (B > (int64_t(1) << 31) / H || T > (int64_t(1) << 31)) return nullptr;
+  if (check_device() != ATTN_OK) return nullptr;
+  if (pick_waves(B, H, T) == 8) return attn_kernel_name(0, d, causal);
+  static const char* names[2][2] = {
+      {"attn_fwd_bf16_d64_full_br128_bc64_w4", "attn_fwd_bf16_d64_causal_br128_bc64_w4"},
+      {"attn_fwd_bf16_d128_full_br128_bc64_w4", "attn_fwd_bf16_d128_causal_br128_bc64_w4"}};
+  return names[d == 128 ? 1 : 0][causal];
 }
 
 const char* attn_kernel_name(int is_f32, int64_t d, int causal) {

@@ -71,6 +71,30 @@ def test_ragged_shapes(T, causal, d, dtype):
     assert eo <= to and el <= tl, (eo, el)
 
 
+# Ragged lengths on grids of at least one 8-wave workgroup per CU (the small
+# shapes above run the 4-wave instance), and the instance choice itself.
+@pytest.mark.parametrize("B,H,T,d,causal", [(2, 64, 1000, 128, True), (2, 64, 1000, 128, False),
+                                            (1, 128, 777, 64, True)])
+def test_ragged_large_grid(B, H, T, d, causal):
+    import exact_attention_123_amd as ea
+    name = ea.fwd_kernel_name_for(B, H, T, d, causal)
+    say(f"ragged large grid B={B} H={H} T={T} d={d} causal={causal}: {name}")
+    assert name is not None and name.endswith("_w8")
+    x = make_qkv(B, H, T, d, dtype="bf16", seed=1500 + T + d + int(causal))
+    scale = 1.0 / math.sqrt(d)
+    O, L = run(x, causal, scale)
+    eo, el = compare(x, O, L, causal, scale)
+    to, tl = TOL["bf16"]
+    assert eo <= to and el <= tl, (eo, el)
+
+
+def test_small_grid_uses_four_waves():
+    import exact_attention_123_amd as ea
+    assert ea.fwd_kernel_name_for(1, 8, 2048, 64, True) == "attn_fwd_bf16_d64_causal_br128_bc64_w4"
+    assert ea.fwd_kernel_name_for(1, 32, 8192, 128, True) == ea.kernel_name(False, 128, True)
+    assert ea.fwd_kernel_name_for(0, 8, 2048, 64, True) is None
+
+
 # ---------------------------------------------------------------------------
 # The five workloads
 # ---------------------------------------------------------------------------
