@@ -247,7 +247,8 @@ __device__ __forceinline__ float sum_tree(const float* x) {
   return (a + b) + (c + d);
 }
 
-// One wave owns 32 query rows; the workgroup (8 waves) 256 rows of one head.
+// One wave owns 32 query rows; the workgroup (NWAVES = 8 waves, or 4 for
+// grids smaller than the GPU) 32 NWAVES rows of one head.
 // Key/value tiles of 64 keys stream through three LDS stages per operand,
 // written by direct-to-LDS buffer loads (no staging registers) three tiles
 // (K) and two tiles (V) ahead of their use, so a load has two tile periods
