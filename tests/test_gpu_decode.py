@@ -4,9 +4,10 @@ oracle on the same seeded inputs.
 Tolerances as for the bf16 forward: max abs error 2e-2 on O and 1e-3 on LSE.
 Cache rows past the valid length hold NaN bit patterns, so any read beyond
 Tk shows up as a non-finite output.  Shapes cover one and several new
-queries, grouped key/value heads (G = 1, 4, 8), caches shorter than one
-block, ragged lengths, a single split and many splits (the cross-split
-merge), and the full decode workloads on sampled heads.
+queries, grouped key/value heads (G = 1, 4, 8), more query rows per
+key/value head than one workgroup takes (up to the 256-row limit), caches
+shorter than one block, ragged lengths, a single split and many splits (the
+cross-split merge), and the full decode workloads on sampled heads.
 """
 import math
 import sys
@@ -57,7 +58,7 @@ def check(x, O, L, causal, scale, Tk, heads=None):
 
 CASES = []
 for Tq, H, Hkv in ((1, 8, 8), (1, 32, 8), (1, 8, 1), (2, 8, 2), (4, 8, 8), (4, 16, 2),
-                   (32, 4, 4), (8, 32, 4), (5, 16, 1), (64, 2, 2)):
+                   (32, 4, 4), (8, 32, 4), (5, 16, 1), (64, 2, 2), (32, 32, 4)):
     for Tk in (1, 7, 33, 100, 1000, 5000):
         if Tk >= Tq:
             CASES.append((Tq, H, Hkv, Tk))
