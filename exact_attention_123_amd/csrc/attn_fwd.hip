@@ -137,12 +137,15 @@ __device__ __forceinline__ float pair_max(float x) {
 // smaller still, so they are negligible either way.
 constexpr float kLazyRescale = 64.0f;
 // Bound on a lane's sum of one sub-tile's weights in the bf16 kernel (see
-// its softmax): above it the running max is raised.  kRegrow: the rows whose
-// sub-tile max outgrows the running max by more than this get a new one
-// (any row whose weights reached the bound did: its largest weight is then
-// above 2^60).
+// its softmax): above it the running max is raised.  kRegrow: once some lane
+// passed the bound, every row whose sub-tile max exceeds its running max by
+// more than this gets the sub-tile max as its new running max (a row that
+// reached the bound always does: its largest weight is then above 2^60).
+// At 0 each such event brings every row of the wave up to date, which makes
+// the next one as late as possible (the event costs the wave the same
+// whatever number of rows it raises).
 constexpr float kMaxLaneSum = 18446744073709551616.0f;  // 2^64
-constexpr float kRegrow = 32.0f;
+constexpr float kRegrow = 0.0f;
 
 // Online-softmax update for one wave's tile of scores ("FlashAttention --
 // avoid writing the giant intermediate", "Tiling and an incremental
@@ -473,8 +476,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   // that bound every weight is at most 2^64 and m may stay where it is (the
   // common factor cancels in acc / l): no row max is needed.
   //
-  // regrow (only when some lane's sum passed the bound, including the first
-  // visible sub-tile, where m is still -1e38 and the weights are inf): the
+  // regrow (only when some lane's sum passed the bound; the workgroup's
+  // first sub-tile, where m is still -1e38, goes straight to it): the
   // row max over the sub-tile (the two lane halves holding a query's scores
   // exchange theirs) becomes the running max of the rows whose max outgrew
   // m by more than kRegrow, the accumulator and normalisers of those rows
@@ -542,10 +545,15 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        pb[a][u] = (__bf16)p[8 * a + u];
-        ws += (float)pb[a][u];
-      }
+      for (int u = 0; u < 8; ++u) pb[a][u] = (__bf16)p[8 * a + u];
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 0, 1), one2, ws,
+                                           false);
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 2, 3), one2, ws,
+                                           false);
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 4, 5), one2, ws,
+                                           false);
+      ws = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 6, 7), one2, ws,
+                                           false);
     }
   };
 
