@@ -185,8 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
       }
       // Register 8 a + e of lane (j, h) holds query i0 + 16 a + 8 h + e and
       // key kw0 + j.
-      const bool edge = (CAUSAL && i0 < kw0 + 31) || kw0 + 31 >= T;
-      bf16x8_t pb[2], db[2];
+      float p[16], g[16];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int q8 = 32 * u + 16 * a + 8 * h;
@@ -198,15 +197,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
         for (int e = 0; e < 8; ++e) {
           const float lse2 = e < 4 ? l0[e] : l1[e - 4];
           const float dl = e < 4 ? d0[e] : d1[e - 4];
-          float p = exp2_hw(fmaf(S[8 * a + e], c, -lse2));
-          if (edge) {
-            const int key = kw0 + j, query = i0 + 16 * a + 8 * h + e;
-            if (key >= T || (CAUSAL && key > query)) p = 0.0f;
-          }
-          pb[a][e] = (__bf16)p;
-          db[a][e] = (__bf16)(p * (dP[8 * a + e] - dl));
+          p[8 * a + e] = exp2_hw(fmaf(S[8 * a + e], c, -lse2));
+          g[8 * a + e] = dP[8 * a + e] - dl;
         }
       }
+      // The mask (keys past the end of the sequence, and causal keys after
+      // the query) only on sub-tiles that need it: the empty asm keeps this
+      // a branch; as a select the compiler would apply it to every tile.
+      if ((CAUSAL && i0 < kw0 + 31) || kw0 + 31 >= T) {
+        asm volatile("" ::: "memory");
+        // key kw0 + j is masked for query i0 + 16 a + 8 h + e iff
+        // 16 a + e < lim (every query when the key is past the end)
+        const int key = kw0 + j;
+        const int lim = key >= T ? 64 : (CAUSAL ? key - i0 - 8 * h : -1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + (r & 7) < lim) p[r] = 0.0f;
+      }
+      bf16x8_t pb[2], db[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[a][e] = (__bf16)p[8 * a + e];
+          db[a][e] = (__bf16)(p[8 * a + e] * g[8 * a + e]);
+        }
       // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 queries.
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
@@ -325,19 +340,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       }
       // Register 8 a + e of lane (j, h) holds key kv0 + 16 a + 8 h + e and
       // query qg.
-      const bool edge = (CAUSAL && kv0 + 31 > qw0) || kv0 + 31 >= T;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(S[r], c, -lse2));
+      // The mask only on sub-tiles that need it (a branch, as in the dK/dV
+      // kernel): key kv0 + 16 a + 8 h + e is masked iff 16 a + e >= lim.
+      if ((CAUSAL && kv0 + 31 > qw0) || kv0 + 31 >= T) {
+        asm volatile("" ::: "memory");
+        const int lim = min(T, CAUSAL ? qg + 1 : T) - kv0 - 8 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + (r & 7) >= lim) p[r] = 0.0f;
+      }
       bf16x8_t db[2];
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float p = exp2_hw(fmaf(S[8 * a + e], c, -lse2));
-          if (edge) {
-            const int key = kv0 + 16 * a + 8 * h + e;
-            if (key >= T || (CAUSAL && key > qg)) p = 0.0f;
-          }
-          db[a][e] = (__bf16)(p * (dP[8 * a + e] - dl));
-        }
+        for (int e = 0; e < 8; ++e) db[a][e] = (__bf16)(p[8 * a + e] * (dP[8 * a + e] - dl));
       // dQ^T += K^T dS^T over the sub-tile's 32 keys.
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
