@@ -464,7 +464,9 @@ def main() -> int:
         fl = ea.bwd_flops(B, H, T, d, causal)
     else:
         do_bits = None
-        kname = ea.kernel_name(dt == "f32", d, causal)
+        # the instance attn_fwd launches for these sizes on this device
+        kname = (ea.kernel_name(True, d, causal) if dt == "f32"
+                 else ea.fwd_kernel_name_for(B, H, T, d, causal))
         knames = [kname]
         fl = ea.flops(B, H, T, d, causal)
 

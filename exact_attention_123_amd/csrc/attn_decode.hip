@@ -41,281 +41,35 @@
 #include <cstring>
 
 #include "attn.h"
+#include "rows.h"
 #include "tiles.h"
 
 namespace {
 
 using namespace attn_tiles;
+using attn_rows::kBlk;
+using attn_rows::kMaxRows;
+using attn_rows::kThreads;
+using attn_rows::kWaves;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBlk = 32;            // keys per block (one MFMA score tile)
-constexpr int kMaxRows = 32;        // query rows of one workgroup (one MFMA column block)
-constexpr int kMaxChunks = 8;       // Tq * G <= 256 query rows per key/value head
+constexpr int kMaxChunks = 8;  // Tq * G <= 256 query rows per key/value head
 // Key split: about kTargetGroups workgroups (one round at two per CU), each
 // split at least kMinSplitKeys long: short splits cost a prologue, an LDS
 // merge and partial results each (measured: 32 splits of 4096 keys read a
 // 131072-key cache at 4.7 TB/s, 128 splits of 1024 keys at 3.3 TB/s).
 constexpr int kMinSplitKeys = 4096;
 constexpr int kTargetGroups = 512;
-// Running-max threshold (log2 units), as in the forward: the max is raised
-// only when a block's max exceeds it by more than this, so weights stay
-// below 2^64 and sums of at most 2^17 of them far inside fp32.
-constexpr float kLazyRescale = 64.0f;
-constexpr float kMinusHuge = -1e38f;
 
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Workgroup (row chunk, kv head bhkv, split s) over keys
-// [s kps, min(Tk, (s + 1) kps)).  Row r < R = Tq G of the group is member
-// r / Tq (query head bhkv G + r / Tq), new query r % Tq; the chunk holds rows
-// 32 chunk .. 32 chunk + 31.  part_o / part_lse: when nsplit > 1,
-// the split's normalised output and natural-log LSE per query row
-// (row index (bhq Tq + qi), NR rows), else unused and O, LSE written.
+// One workgroup per (row chunk, key/value head, key split); see
+// attn_rows::row_chunk_attention.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ part_o,
     float* __restrict__ part_lse, int Tq, int Tk, int Tcap, int G, int nsplit, int kps,
     int NR, int nwg, float c) {
-  using C = RowTile<D>;
-  constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
-  constexpr int TB = kBlk * RB;  // bytes of one K or V block
-  // Two V stages per wave, each stage its own object so that the compiler
-  // can tell the loads into one from the reads of the other.
-  __shared__ __attribute__((aligned(1024))) char sV0[kWaves][TB];
-  __shared__ __attribute__((aligned(1024))) char sV1[kWaves][TB];
-  __shared__ float sM[kWaves][kMaxRows], sL[kWaves][kMaxRows], sW[kWaves][kMaxRows];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = lane & 31, h = lane >> 5;
-  // Workgroup id: row chunk outermost (nwg = B H_kv nsplit workgroups per
-  // chunk), so the chunks reading the same keys share an XCD when nwg is a
-  // multiple of 8.
-  const int id = blockIdx.x;
-  const int chunk = id / nwg, rest = id % nwg;
-  const int bhkv = rest / nsplit, split = rest % nsplit;
-  const int R = Tq * G;             // query rows of the group
-  const int r0 = kMaxRows * chunk;  // this workgroup's first row
-  const bool row_ok = r0 + j < R;
-  const int qi = (r0 + j) % Tq;
-  const size_t qrow = ((size_t)bhkv * G + (r0 + j) / Tq) * Tq + qi;  // global query row
-  const int pos = Tk - Tq + qi;                                      // its position
-
-  // Q fragment: B operand [d][query] of S^T = K Q^T.  The contraction
-  // over d takes k-step s of lane half h from d = 8 (NDS h + s) .. + 8, so
-  // that a lane's K operand over all steps is one contiguous run of its row.
-  bf16x8_t qf[NDS];
-#pragma unroll
-  for (int s = 0; s < NDS; ++s) {
-    qf[s] = bf16x8_t{};
-    if (row_ok)
-      qf[s] = *reinterpret_cast<const bf16x8_t*>(Q + qrow * D + 8 * (NDS * h + s));
-  }
-
-  const int k_lo = split * kps, k_hi = min(Tk, k_lo + kps);
-  const int nblk = (k_hi - k_lo + kBlk - 1) / kBlk;
-  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
-  const __bf16* Kh = K + (size_t)bhkv * Tcap * D;
-  const __bf16* Vh = V + (size_t)bhkv * Tcap * D;
-
-  TileAddr<D> ad;
-  ad.init(lane);
-  TileDma<D, kBlk, 1> dma;
-  dma.init(0, lane);
-  constexpr int PER = TileDma<D, kBlk, 1>::PER;  // V load instructions per block
-  // K operand of lane (j, h): row row_perm(j) of the block, d from
-  // 8 NDS h on (see qf).  Keys >= k_hi read as zero (and are masked below).
-  const int krow = row_perm(j) * RB + 16 * NDS * h;
-  auto load = [&](bf16x8_t (&kr)[NDS], char* vt, int i) __attribute__((always_inline)) {
-    const int kb0 = k_lo + kBlk * (wave + kWaves * i);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb0 * D, max(k_hi - kb0, 0) * RB);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int s = 0; s < NDS; ++s)
-      kr[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rk, krow + 16 * s));
-    dma.load(vt, Vh, k_hi, kb0, 0);
-  };
-
-  f32x16_t oacc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
-  float m_run = kMinusHuge, l_run = 0.0f, w_run = 0.0f;
-  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // One block: scores, mask, online softmax, O^T += V^T P^T.
-  auto block = [&](const bf16x8_t (&kr)[NDS], const char* vt, int i)
-      __attribute__((always_inline)) {
-    const int kb0 = k_lo + kBlk * (wave + kWaves * i);
-    f32x16_t sc = f32x16_t{};
-#pragma unroll
-    for (int s = 0; s < NDS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], qf[s], sc, 0, 0, 0);
-    // scores in log2 units (any sign of the scale); register 8 a + e holds
-    // key kb0 + 16 a + 8 h + e of query row j
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] *= c;
-    if (kb0 + kBlk > k_hi || (CAUSAL && kb0 + kBlk - 1 > Tk - Tq)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb0 + 16 * (r >> 3) + 8 * h + (r & 7);
-        if (key >= k_hi || (CAUSAL && key > pos)) sc[r] = -INFINITY;
-      }
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-    const float mt = pair_max(mx);
-    const bool grow = mt > m_run + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float alpha = grow ? exp2_hw(m_run - mt) : 1.0f;
-      l_run *= alpha;
-      w_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      m_run = grow ? mt : m_run;
-    }
-    bf16x8_t pb[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2_hw(sc[8 * a + e] - m_run);
-        l_run += p;
-        pb[a][e] = (__bf16)p;
-      }
-#pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      // the normaliser of O sums exactly the bf16 weights the MFMA uses
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 0, 1), one2,
-                                             w_run, false);
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 2, 3), one2,
-                                             w_run, false);
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 4, 5), one2,
-                                             w_run, false);
-      w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 6, 7), one2,
-                                             w_run, false);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            lds_tr(vt, 16 * a * RB + ad.tr[0][dt], 16 * a * RB + ad.tr[1][dt]), pb[a],
-            oacc[dt], 0, 0, 0);
-    }
-  };
-  // Waits until at most n of this wave's loads are in flight (loads
-  // complete in issue order; a direct-to-LDS load has written LDS when it
-  // completes).
-  auto wait_loads = [&](auto n) __attribute__((always_inline)) {
-    constexpr int N = decltype(n)::value;
-    static_assert(N < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-    asm volatile("" ::: "memory");
-  };
-  using Zero = std::integral_constant<int, 0>;
-  using Next = std::integral_constant<int, NDS + PER>;  // one block's loads
-
-  bf16x8_t k0[NDS], k1[NDS];
-  if (nmine > 0) load(k0, sV0[wave], 0);
-  for (int i = 0; i < nmine; i += 2) {
-    if (i + 1 < nmine) {
-      load(k1, sV1[wave], i + 1);
-      wait_loads(Next{});
-    } else {
-      wait_loads(Zero{});
-    }
-    block(k0, sV0[wave], i);
-    if (i + 1 >= nmine) break;
-    if (i + 2 < nmine) {
-      load(k0, sV0[wave], i + 2);
-      wait_loads(Next{});
-    } else {
-      wait_loads(Zero{});
-    }
-    block(k1, sV1[wave], i + 1);
-  }
-
-  // Merge the four waves' partial results for each query row.
-  l_run += __shfl_xor(l_run, 32);
-  w_run += __shfl_xor(w_run, 32);
-  __syncthreads();  // every wave is done with its LDS stages
-  // Wave w's 32 x D fp32 accumulator goes to half (w & 1) of sV0 (w < 2)
-  // or sV1 (w >= 2): each V stage holds exactly two of them.
-  static_assert(sizeof(sV0) == 2 * sizeof(float) * kMaxRows * D, "merge buffer");
-  auto part = [&](int w) __attribute__((always_inline)) -> float* {
-    return reinterpret_cast<float*>(w < 2 ? &sV0[0][0] : &sV1[0][0]) + (w & 1) * kMaxRows * D;
-  };
-  {
-    float* mine = part(wave);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4_t v4;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v4[u] = oacc[dt][4 * g + u];
-        *reinterpret_cast<f32x4_t*>(&mine[j * D + 32 * dt + 8 * g + 4 * h]) = v4;
-      }
-  }
-  if (h == 0) {
-    sM[wave][j] = m_run;
-    sL[wave][j] = l_run;
-    sW[wave][j] = w_run;
-  }
-  __syncthreads();
-
-  // 8 threads per query row, D / 8 columns each.
-  constexpr int CPT = D / 8;
-  const int row = tid >> 3, c0 = (tid & 7) * CPT;
-  if (r0 + row >= R) return;
-  float M = sM[0][row];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sM[w][row]);
-  float a[kWaves], Lt = 0.0f, Wt = 0.0f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    a[w] = exp2_hw(sM[w][row] - M);
-    Lt += a[w] * sL[w][row];
-    Wt += a[w] * sW[w][row];
-  }
-  // A row with no visible key in this split (causal, split past its
-  // position) has Wt = 0: output 0, LSE -inf, weight 0 in the merge.
-  const float inv = Wt > 0.0f ? 1.0f / Wt : 0.0f;
-  float o[CPT];
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      acc = fmaf(a[w], part(w)[row * D + c0 + u], acc);
-    o[u] = acc * inv;
-  }
-  const float lse = Lt > 0.0f ? (M + log2_hw(Lt)) * kLn2 : -INFINITY;
-  const size_t orow = ((size_t)bhkv * G + (r0 + row) / Tq) * Tq + (r0 + row) % Tq;
-  if (nsplit == 1) {
-#pragma unroll
-    for (int u = 0; u < CPT; u += 4) {
-      __bf16 b4[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) b4[x] = (__bf16)o[u + x];
-      u32x2_t bits;
-      std::memcpy(&bits, b4, 8);
-      *reinterpret_cast<u32x2_t*>(O + orow * D + c0 + u) = bits;
-    }
-    if (c0 == 0) LSE[orow] = lse;
-  } else {
-    float* dst = part_o + ((size_t)split * NR + orow) * D + c0;
-#pragma unroll
-    for (int u = 0; u < CPT; u += 4)
-      *reinterpret_cast<f32x4_t*>(dst + u) = f32x4_t{o[u], o[u + 1], o[u + 2], o[u + 3]};
-    if (c0 == 0) part_lse[(size_t)split * NR + orow] = lse;
-  }
+  attn_rows::row_chunk_attention<D, CAUSAL>(Q, K, V, O, LSE, part_o, part_lse, Tq, Tk, Tcap, G,
+                                            nsplit, kps, NR, nwg, c);
 }
 
 // Merge of the splits: one wave per query row, D / 64 columns per lane.

@@ -240,16 +240,21 @@ const char* attn_status_string(attn_status s);
  * (is_f32 = 1) launches for head dimension d and the causal flag, e.g.
  * "attn_fwd_bf16_d128_causal_br256_bc64_w8", so that a caller can log which
  * kernel ran.  For bf16 this is the instance of grids with at least one
- * workgroup per CU (see attn_fwd_kernel_name_for).  NULL if the combination
+ * 256-row workgroup per CU (smaller grids: see attn_fwd_kernel_name_for).  NULL if the combination
  * is unsupported.
  */
 const char* attn_kernel_name(int is_f32, int64_t d, int causal);
 
 /*
  * Name of the kernel instance attn_fwd / attn_fwd_gqa launch for these sizes
- * on the current device: the 8-wave instance (256 query rows per workgroup)
- * unless B * H * ceil(T / 256) is below the device's CU count, then the
- * 4-wave one (128 rows, e.g. "attn_fwd_bf16_d64_causal_br128_bc64_w4").
+ * on the current device (B * H query heads):
+ *   - the row-chunk kernel (32 query rows per workgroup, their keys split
+ *     over 4 waves, e.g. "attn_fwd_rows_bf16_d64_causal_br32_bc32_w4") when
+ *     B * H * ceil(T / 128) * (d / 64) is at most the device's CU count;
+ *   - else the 4-wave instance (128 rows, e.g.
+ *     "attn_fwd_bf16_d128_causal_br128_bc64_w4") when B * H * ceil(T / 256)
+ *     is below the CU count;
+ *   - else the 8-wave instance (256 query rows per workgroup).
  * NULL if the sizes are unsupported or the current device is not a gfx950.
  */
 const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T,

@@ -72,7 +72,7 @@ def test_ragged_shapes(T, causal, d, dtype):
 
 
 # Ragged lengths on grids of at least one 8-wave workgroup per CU (the small
-# shapes above run the 4-wave instance), and the instance choice itself.
+# shapes above run the row-chunk kernel), and the instance choice itself.
 @pytest.mark.parametrize("B,H,T,d,causal", [(2, 64, 1000, 128, True), (2, 64, 1000, 128, False),
                                             (1, 128, 777, 64, True)])
 def test_ragged_large_grid(B, H, T, d, causal):
@@ -88,9 +88,37 @@ def test_ragged_large_grid(B, H, T, d, causal):
     assert eo <= to and el <= tl, (eo, el)
 
 
-def test_small_grid_uses_four_waves():
+# Shapes between the two small-grid rules run the 4-wave instance: ragged
+# and aligned lengths, both masks.
+@pytest.mark.parametrize("B,H,T,d,causal", [(1, 8, 4000, 128, True), (1, 8, 4096, 128, False),
+                                            (2, 4, 3000, 128, True)])
+def test_four_wave_instance(B, H, T, d, causal):
     import exact_attention_123_amd as ea
-    assert ea.fwd_kernel_name_for(1, 8, 2048, 64, True) == "attn_fwd_bf16_d64_causal_br128_bc64_w4"
+    name = ea.fwd_kernel_name_for(B, H, T, d, causal)
+    say(f"4-wave instance B={B} H={H} T={T} d={d} causal={causal}: {name}")
+    assert name is not None and name.endswith("_br128_bc64_w4")
+    seed = 1700 + T + d + int(causal)
+    x = make_qkv(B, H, T, d, dtype="bf16", seed=seed)
+    scale = 1.0 / math.sqrt(d)
+    O, L = run(x, causal, scale)
+    eo, el = compare(x, O, L, causal, scale,
+                     rows_for=lambda b, h: boundary_rows(T, 64, seed + 31 * b + h),
+                     full_heads={(0, 0), (B - 1, H - 1)})
+    to, tl = TOL["bf16"]
+    assert eo <= to and el <= tl, (eo, el)
+
+
+def test_small_grid_uses_row_chunks():
+    """Problems too small to fill the GPU with 256-row workgroups take the
+    row-chunk kernel when the 4-wave grid (in d = 64 units) fits the CUs
+    once, else the 4-wave kernel."""
+    import exact_attention_123_amd as ea
+    assert (ea.fwd_kernel_name_for(1, 8, 2048, 64, True)
+            == "attn_fwd_rows_bf16_d64_causal_br32_bc32_w4")
+    assert (ea.fwd_kernel_name_for(1, 1, 16384, 128, True)
+            == "attn_fwd_rows_bf16_d128_causal_br32_bc32_w4")
+    assert (ea.fwd_kernel_name_for(1, 8, 4096, 128, False)
+            == "attn_fwd_bf16_d128_full_br128_bc64_w4")
     assert ea.fwd_kernel_name_for(1, 32, 8192, 128, True) == ea.kernel_name(False, 128, True)
     assert ea.fwd_kernel_name_for(0, 8, 2048, 64, True) is None
 
