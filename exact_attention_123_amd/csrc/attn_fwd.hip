@@ -919,30 +919,46 @@ FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d) {
 }
 
 // Square forward on the row-chunk kernel: Tq = Tk = T, one key split (the
-// chunk's keys are cut only between its waves), O and LSE written directly.
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(attn_rows::kThreads, 2) void attn_fwd_rows_kernel(
+// chunk's keys are cut only between its NW waves), O and LSE written
+// directly.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_fwd_rows_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int G, int NR, int nwg, float c) {
-  attn_rows::row_chunk_attention<D, CAUSAL>(Q, K, V, O, LSE, nullptr, nullptr, T, T, T, G, 1, T,
-                                            NR, nwg, c);
+  attn_rows::row_chunk_attention<D, CAUSAL, NW>(Q, K, V, O, LSE, nullptr, nullptr, T, T, T, G, 1,
+                                                T, NR, nwg, c);
 }
+
+template <int NW>
+const void* rows_kernel(int64_t d, int causal) {
+  if (d == 64) return causal ? (const void*)attn_fwd_rows_kernel<64, true, NW>
+                             : (const void*)attn_fwd_rows_kernel<64, false, NW>;
+  return causal ? (const void*)attn_fwd_rows_kernel<128, true, NW>
+                : (const void*)attn_fwd_rows_kernel<128, false, NW>;
+}
+
+// Waves of the row-chunk kernel: 4, or 8 for sequences of at least 4096
+// keys.  The kernel's time is mostly the chunks re-reading their keys from
+// L2, which more waves do not change; only long key ranges gain from the
+// shorter per-wave chain.  Measured on MI355X (us per launch, 8 / 4
+// waves): B H = 1, T = 16384, d = 128, causal 167 / 217; B H = 4, T = 4096,
+// d = 128, causal 55 / 61; B H = 8, T = 4096, d = 64, causal 56 / 56; but
+// B H = 8, T = 2048, d = 64, causal 24 / 20 and B H = 16, T = 1024,
+// d = 128, no mask 35 / 28.
+int rows_waves(int64_t T) { return T >= 4096 ? 8 : 4; }
 
 attn_status launch_rows(int64_t d, int causal, const void* q, const void* k, const void* v,
                         void* o, float* lse, int64_t B, int64_t H, int64_t Hkv, int64_t T,
                         float scale, hipStream_t stream) {
-  const void* kern =
-      d == 64 ? (causal ? (const void*)attn_fwd_rows_kernel<64, true>
-                        : (const void*)attn_fwd_rows_kernel<64, false>)
-              : (causal ? (const void*)attn_fwd_rows_kernel<128, true>
-                        : (const void*)attn_fwd_rows_kernel<128, false>);
+  const int nw = rows_waves(T);
+  const void* kern = nw == 8 ? rows_kernel<8>(d, causal) : rows_kernel<4>(d, causal);
   const int64_t G = H / Hkv;
   const int64_t nchunk = (T * G + attn_rows::kMaxRows - 1) / attn_rows::kMaxRows;
   int t = (int)T, g = (int)G, nr = (int)(B * H * T), nwg = (int)(B * Hkv);
   float c = scale * kLog2e;
   void* args[] = {(void*)&q, (void*)&k,  (void*)&v,   (void*)&o,   (void*)&lse,
                   (void*)&t, (void*)&g,  (void*)&nr,  (void*)&nwg, (void*)&c};
-  const dim3 grid((unsigned)(B * Hkv * nchunk)), block(attn_rows::kThreads);
+  const dim3 grid((unsigned)(B * Hkv * nchunk)), block(64 * nw);
   if (hipLaunchKernel(kern, grid, block, args, 0, stream) != hipSuccess) return ATTN_ERR_LAUNCH;
   return ATTN_OK;
 }
@@ -1046,11 +1062,15 @@ const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d,
   static const char* w4[2][2] = {
       {"attn_fwd_bf16_d64_full_br128_bc64_w4", "attn_fwd_bf16_d64_causal_br128_bc64_w4"},
       {"attn_fwd_bf16_d128_full_br128_bc64_w4", "attn_fwd_bf16_d128_causal_br128_bc64_w4"}};
-  static const char* rows[2][2] = {
-      {"attn_fwd_rows_bf16_d64_full_br32_bc32_w4", "attn_fwd_rows_bf16_d64_causal_br32_bc32_w4"},
-      {"attn_fwd_rows_bf16_d128_full_br32_bc32_w4",
-       "attn_fwd_rows_bf16_d128_causal_br32_bc32_w4"}};
-  return (plan == FwdPlan::kRows ? rows : w4)[d == 128 ? 1 : 0][causal];
+  static const char* rows[2][2][2] = {
+      {{"attn_fwd_rows_bf16_d64_full_br32_bc32_w4", "attn_fwd_rows_bf16_d64_causal_br32_bc32_w4"},
+       {"attn_fwd_rows_bf16_d128_full_br32_bc32_w4",
+        "attn_fwd_rows_bf16_d128_causal_br32_bc32_w4"}},
+      {{"attn_fwd_rows_bf16_d64_full_br32_bc32_w8", "attn_fwd_rows_bf16_d64_causal_br32_bc32_w8"},
+       {"attn_fwd_rows_bf16_d128_full_br32_bc32_w8",
+        "attn_fwd_rows_bf16_d128_causal_br32_bc32_w8"}}};
+  if (plan == FwdPlan::kRows) return rows[rows_waves(T) == 8 ? 1 : 0][d == 128 ? 1 : 0][causal];
+  return w4[d == 128 ? 1 : 0][causal];
 }
 
 const char* attn_kernel_name(int is_f32, int64_t d, int causal) {

@@ -1,6 +1,6 @@
 // Row-chunk attention for AMD Instinct MI355X (gfx950): one workgroup takes
 // up to 32 query rows (one MFMA column block) and a range of keys, which its
-// four waves split between them: each wave streams its own 32-key blocks,
+// waves (4 or 8) split between them: each wave streams its own 32-key blocks,
 // with no workgroup barrier in the loop -- K straight into registers (the A
 // operand of the score MFMA as loaded), V direct-to-LDS (its transposing
 // read needs LDS), both one block ahead -- and the waves' partial results
@@ -20,7 +20,7 @@
 // Used by the decode kernel (key splits over workgroups, merged by a second
 // kernel) and by the forward for grids too small to fill the GPU with
 // 256-row workgroups (one split: the keys of a chunk are cut only between
-// its waves, so the critical path is a quarter of the longest key range).
+// its waves, so the critical path is 1 / NW of the longest key range).
 #ifndef ATTN_ROWS_H_
 #define ATTN_ROWS_H_
 
@@ -36,7 +36,7 @@ namespace attn_rows {
 
 using namespace attn_tiles;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;  // waves per workgroup unless the caller picks NW
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;      // keys per block (one MFMA score tile)
 constexpr int kMaxRows = 32;  // query rows of one workgroup (one MFMA column block)
@@ -52,14 +52,15 @@ __device__ __forceinline__ float pair_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Body of a kernel of kThreads threads.  Workgroup (row chunk, kv head
+// Body of a kernel of 64 NW threads (NW waves share the keys of the
+// chunk).  Workgroup (row chunk, kv head
 // bhkv, split s) over keys [s kps, min(Tk, (s + 1) kps)); the grid holds
 // nwg = (key/value heads) x nsplit workgroups per chunk, chunk outermost.
 // The chunk holds rows 32 chunk .. 32 chunk + 31 of the R = Tq G rows of
 // its group.  part_o / part_lse: when nsplit > 1, the split's normalised
 // output and natural-log LSE per query row (row index (bhq Tq + qi), NR
 // rows), else unused and O, LSE written.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int NW = kWaves>
 __device__ __forceinline__ void row_chunk_attention(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ part_o,
@@ -70,9 +71,10 @@ __device__ __forceinline__ void row_chunk_attention(
   constexpr int TB = kBlk * RB;  // bytes of one K or V block
   // Two V stages per wave, each stage its own object so that the compiler
   // can tell the loads into one from the reads of the other.
-  __shared__ __attribute__((aligned(1024))) char sV0[kWaves][TB];
-  __shared__ __attribute__((aligned(1024))) char sV1[kWaves][TB];
-  __shared__ float sM[kWaves][kMaxRows], sL[kWaves][kMaxRows], sW[kWaves][kMaxRows];
+  static_assert(NW % 2 == 0 && (64 * NW) % kMaxRows == 0, "wave count");
+  __shared__ __attribute__((aligned(1024))) char sV0[NW][TB];
+  __shared__ __attribute__((aligned(1024))) char sV1[NW][TB];
+  __shared__ float sM[NW][kMaxRows], sL[NW][kMaxRows], sW[NW][kMaxRows];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -118,7 +120,7 @@ __device__ __forceinline__ void row_chunk_attention(
     k_all = Tk - Tq + qi_min + 1;
   }
   const int nblk = (k_hi - k_lo + kBlk - 1) / kBlk;
-  const int nmine = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;
+  const int nmine = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
   const __bf16* Kh = K + (size_t)bhkv * Tcap * D;
   const __bf16* Vh = V + (size_t)bhkv * Tcap * D;
 
@@ -131,7 +133,7 @@ __device__ __forceinline__ void row_chunk_attention(
   // 8 NDS h on (see qf).  Keys >= k_hi read as zero (and are masked below).
   const int krow = row_perm(j) * RB + 16 * NDS * h;
   auto load = [&](bf16x8_t (&kr)[NDS], char* vt, int i) __attribute__((always_inline)) {
-    const int kb0 = k_lo + kBlk * (wave + kWaves * i);
+    const int kb0 = k_lo + kBlk * (wave + NW * i);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb0 * D, max(k_hi - kb0, 0) * RB);
     asm volatile("" ::: "memory");
 #pragma unroll
@@ -149,7 +151,7 @@ __device__ __forceinline__ void row_chunk_attention(
   // One block: scores, mask, online softmax, O^T += V^T P^T.
   auto block = [&](const bf16x8_t (&kr)[NDS], const char* vt, int i)
       __attribute__((always_inline)) {
-    const int kb0 = k_lo + kBlk * (wave + kWaves * i);
+    const int kb0 = k_lo + kBlk * (wave + NW * i);
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int s = 0; s < NDS; ++s)
@@ -239,15 +241,16 @@ __device__ __forceinline__ void row_chunk_attention(
     block(k1, sV1[wave], i + 1);
   }
 
-  // Merge the four waves' partial results for each query row.
+  // Merge the waves' partial results for each query row.
   l_run += __shfl_xor(l_run, 32);
   w_run += __shfl_xor(w_run, 32);
   __syncthreads();  // every wave is done with its LDS stages
-  // Wave w's 32 x D fp32 accumulator goes to half (w & 1) of sV0 (w < 2)
-  // or sV1 (w >= 2): each V stage holds exactly two of them.
-  static_assert(sizeof(sV0) == 2 * sizeof(float) * kMaxRows * D, "merge buffer");
+  // Wave w's 32 x D fp32 accumulator goes to slot w % (NW / 2) of sV0
+  // (w < NW / 2) or sV1: each V stage holds exactly NW / 2 of them.
+  static_assert(sizeof(sV0) == NW / 2 * sizeof(float) * kMaxRows * D, "merge buffer");
   auto part = [&](int w) __attribute__((always_inline)) -> float* {
-    return reinterpret_cast<float*>(w < 2 ? &sV0[0][0] : &sV1[0][0]) + (w & 1) * kMaxRows * D;
+    return reinterpret_cast<float*>(w < NW / 2 ? &sV0[0][0] : &sV1[0][0]) +
+           (w % (NW / 2)) * kMaxRows * D;
   };
   {
     float* mine = part(wave);
@@ -268,16 +271,18 @@ __device__ __forceinline__ void row_chunk_attention(
   }
   __syncthreads();
 
-  // 8 threads per query row, D / 8 columns each.
-  constexpr int CPT = D / 8;
-  const int row = tid >> 3, c0 = (tid & 7) * CPT;
+  // TPR threads per query row, CPT columns each.
+  constexpr int TPR = 64 * NW / kMaxRows;  // threads per query row
+  constexpr int CPT = D / TPR;             // columns per thread
+  static_assert(CPT % 4 == 0, "columns per thread");
+  const int row = tid / TPR, c0 = (tid % TPR) * CPT;
   if (r0 + row >= R) return;
   float M = sM[0][row];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sM[w][row]);
-  float a[kWaves], Lt = 0.0f, Wt = 0.0f;
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sM[w][row]);
+  float a[NW], Lt = 0.0f, Wt = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     a[w] = exp2_hw(sM[w][row] - M);
     Lt += a[w] * sL[w][row];
     Wt += a[w] * sW[w][row];
@@ -290,7 +295,7 @@ __device__ __forceinline__ void row_chunk_attention(
   for (int u = 0; u < CPT; ++u) {
     float acc = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < NW; ++w)
       acc = fmaf(a[w], part(w)[row * D + c0 + u], acc);
     o[u] = acc * inv;
   }

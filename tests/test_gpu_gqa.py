@@ -56,6 +56,23 @@ def test_gqa_forward(T, H, Hkv, causal, d):
     assert np.abs(L - Lref).max() <= 1e-3
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_gqa_forward_row_chunks_long(causal):
+    """Grouped heads on the row-chunk kernel with 8 waves (a small grid of a
+    long sequence): 32-row chunks of the group's rows, keys split 8 ways."""
+    import exact_attention_123_amd as ea
+    B, H, Hkv, T, d = 1, 4, 2, 4500, 64
+    assert ea.fwd_kernel_name_for(B, H, T, d, causal).endswith("_w8")
+    say(f"[gqa fwd rows] T={T} H={H} Hkv={Hkv} causal={causal} d={d}")
+    scale = 1.0 / math.sqrt(d)
+    x = make_qkv(B, H, T, d, seed=6100 + int(causal), qk_mult=2.0, H_kv=Hkv)
+    _, O, L = gpu_fwd(x, causal, scale)
+    Oref, Lref = oracle.attention_gqa(x.q64(), x.k64(), x.v64(), causal=causal, scale=scale)
+    assert np.isfinite(O).all()
+    assert np.abs(O - Oref).max() <= 2e-2
+    assert np.abs(L - Lref).max() <= 1e-3
+
+
 def check_bwd(x, do_bits, dQ, dK, dV, O_used, causal, scale, b, g, keys=None, ub=U):
     """Gradients of key/value head (b, g) and of its query heads against the
     oracle under the per-element bound (rows: the query heads' sampled keys

@@ -108,6 +108,25 @@ def test_four_wave_instance(B, H, T, d, causal):
     assert eo <= to and el <= tl, (eo, el)
 
 
+# Long sequences on grids too small for 256-row workgroups run the
+# row-chunk kernel with 8 waves splitting the keys.
+@pytest.mark.parametrize("B,H,T,d,causal", [(1, 1, 16384, 128, True), (1, 2, 4100, 64, False),
+                                            (1, 2, 4100, 64, True)])
+def test_row_chunk_eight_waves(B, H, T, d, causal):
+    import exact_attention_123_amd as ea
+    name = ea.fwd_kernel_name_for(B, H, T, d, causal)
+    say(f"row-chunk 8 waves B={B} H={H} T={T} d={d} causal={causal}: {name}")
+    assert name is not None and name.startswith("attn_fwd_rows_") and name.endswith("_w8")
+    seed = 1800 + T + d + int(causal)
+    x = make_qkv(B, H, T, d, dtype="bf16", seed=seed)
+    scale = 1.0 / math.sqrt(d)
+    O, L = run(x, causal, scale)
+    eo, el = compare(x, O, L, causal, scale,
+                     rows_for=lambda b, h: boundary_rows(T, 96, seed + 31 * b + h))
+    to, tl = TOL["bf16"]
+    assert eo <= to and el <= tl, (eo, el)
+
+
 def test_small_grid_uses_row_chunks():
     """Problems too small to fill the GPU with 256-row workgroups take the
     row-chunk kernel when the 4-wave grid (in d = 64 units) fits the CUs
@@ -116,7 +135,9 @@ def test_small_grid_uses_row_chunks():
     assert (ea.fwd_kernel_name_for(1, 8, 2048, 64, True)
             == "attn_fwd_rows_bf16_d64_causal_br32_bc32_w4")
     assert (ea.fwd_kernel_name_for(1, 1, 16384, 128, True)
-            == "attn_fwd_rows_bf16_d128_causal_br32_bc32_w4")
+            == "attn_fwd_rows_bf16_d128_causal_br32_bc32_w8")
+    assert (ea.fwd_kernel_name_for(1, 2, 1000, 128, False)
+            == "attn_fwd_rows_bf16_d128_full_br32_bc32_w4")
     assert (ea.fwd_kernel_name_for(1, 8, 4096, 128, False)
             == "attn_fwd_bf16_d128_full_br128_bc64_w4")
     assert ea.fwd_kernel_name_for(1, 32, 8192, 128, True) == ea.kernel_name(False, 128, True)
