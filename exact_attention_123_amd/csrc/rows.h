@@ -60,7 +60,13 @@ __device__ __forceinline__ float pair_max(float x) {
 // its group.  part_o / part_lse: when nsplit > 1, the split's normalised
 // output and natural-log LSE per query row (row index (bhq Tq + qi), NR
 // rows), else unused and O, LSE written.
-template <int D, bool CAUSAL, int NW = kWaves>
+// KLDS: K goes through LDS like V (coalesced direct-to-LDS loads, swizzled
+// row reads) instead of straight into registers.  Loading K in MFMA operand
+// order makes every load instruction touch 64 partial cache lines, which
+// costs the vector memory pipeline four times the work of a coalesced load:
+// the right trade when the kernel streams a long cache from HBM (decode),
+// not when it re-reads short key ranges from L2 (forward on small grids).
+template <int D, bool CAUSAL, int NW = kWaves, bool KLDS = false>
 __device__ __forceinline__ void row_chunk_attention(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ part_o,
@@ -74,6 +80,8 @@ __device__ __forceinline__ void row_chunk_attention(
   static_assert(NW % 2 == 0 && (64 * NW) % kMaxRows == 0, "wave count");
   __shared__ __attribute__((aligned(1024))) char sV0[NW][TB];
   __shared__ __attribute__((aligned(1024))) char sV1[NW][TB];
+  __shared__ __attribute__((aligned(1024))) char sK0[KLDS ? NW : 1][KLDS ? TB : 16];
+  __shared__ __attribute__((aligned(1024))) char sK1[KLDS ? NW : 1][KLDS ? TB : 16];
   __shared__ float sM[NW][kMaxRows], sL[NW][kMaxRows], sW[NW][kMaxRows];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -95,13 +103,15 @@ __device__ __forceinline__ void row_chunk_attention(
 
   // Q fragment: B operand [d][query] of S^T = K Q^T.  The contraction
   // over d takes k-step s of lane half h from d = 8 (NDS h + s) .. + 8, so
-  // that a lane's K operand over all steps is one contiguous run of its row.
+  // that a lane's K operand over all steps is one contiguous run of its row
+  // (K from LDS: d = 8 (2 s + h) .. + 8, the order of the swizzled row
+  // reads).
   bf16x8_t qf[NDS];
 #pragma unroll
   for (int s = 0; s < NDS; ++s) {
     qf[s] = bf16x8_t{};
-    if (row_ok)
-      qf[s] = *reinterpret_cast<const bf16x8_t*>(Q + qrow * D + 8 * (NDS * h + s));
+    const int d0 = KLDS ? 8 * (2 * s + h) : 8 * (NDS * h + s);
+    if (row_ok) qf[s] = *reinterpret_cast<const bf16x8_t*>(Q + qrow * D + d0);
   }
 
   const int k_lo = split * kps;
@@ -132,13 +142,20 @@ __device__ __forceinline__ void row_chunk_attention(
   // K operand of lane (j, h): row row_perm(j) of the block, d from
   // 8 NDS h on (see qf).  Keys >= k_hi read as zero (and are masked below).
   const int krow = row_perm(j) * RB + 16 * NDS * h;
-  auto load = [&](bf16x8_t (&kr)[NDS], char* vt, int i) __attribute__((always_inline)) {
+  auto load = [&](bf16x8_t (&kr)[NDS], char* kt, char* vt, int i) __attribute__((always_inline)) {
     const int kb0 = k_lo + kBlk * (wave + NW * i);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)kb0 * D, max(k_hi - kb0, 0) * RB);
+    // (no load of the next block may move above the reads of the previous
+    // one from the same stage)
     asm volatile("" ::: "memory");
+    if constexpr (KLDS) {
+      dma.load(kt, Kh, k_hi, kb0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rk =
+          make_rsrc(Kh + (size_t)kb0 * D, max(k_hi - kb0, 0) * RB);
 #pragma unroll
-    for (int s = 0; s < NDS; ++s)
-      kr[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rk, krow + 16 * s));
+      for (int s = 0; s < NDS; ++s)
+        kr[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rk, krow + 16 * s));
+    }
     dma.load(vt, Vh, k_hi, kb0, 0);
   };
 
@@ -149,13 +166,14 @@ __device__ __forceinline__ void row_chunk_attention(
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // One block: scores, mask, online softmax, O^T += V^T P^T.
-  auto block = [&](const bf16x8_t (&kr)[NDS], const char* vt, int i)
+  auto block = [&](const bf16x8_t (&kr)[NDS], const char* kt, const char* vt, int i)
       __attribute__((always_inline)) {
     const int kb0 = k_lo + kBlk * (wave + NW * i);
     f32x16_t sc = f32x16_t{};
 #pragma unroll
     for (int s = 0; s < NDS; ++s)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s], qf[s], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KLDS ? lds_row(kt, ad.row[s]) : kr[s], qf[s],
+                                                   sc, 0, 0, 0);
     // scores in log2 units (any sign of the scale); register 8 a + e holds
     // key kb0 + 16 a + 8 h + e of query row j
 #pragma unroll
@@ -219,26 +237,29 @@ __device__ __forceinline__ void row_chunk_attention(
     asm volatile("" ::: "memory");
   };
   using Zero = std::integral_constant<int, 0>;
-  using Next = std::integral_constant<int, NDS + PER>;  // one block's loads
+  // one block's loads
+  using Next = std::integral_constant<int, KLDS ? 2 * PER : NDS + PER>;
 
   bf16x8_t k0[NDS], k1[NDS];
-  if (nmine > 0) load(k0, sV0[wave], 0);
+  char* kt0 = KLDS ? sK0[KLDS ? wave : 0] : nullptr;
+  char* kt1 = KLDS ? sK1[KLDS ? wave : 0] : nullptr;
+  if (nmine > 0) load(k0, kt0, sV0[wave], 0);
   for (int i = 0; i < nmine; i += 2) {
     if (i + 1 < nmine) {
-      load(k1, sV1[wave], i + 1);
+      load(k1, kt1, sV1[wave], i + 1);
       wait_loads(Next{});
     } else {
       wait_loads(Zero{});
     }
-    block(k0, sV0[wave], i);
+    block(k0, kt0, sV0[wave], i);
     if (i + 1 >= nmine) break;
     if (i + 2 < nmine) {
-      load(k0, sV0[wave], i + 2);
+      load(k0, kt0, sV0[wave], i + 2);
       wait_loads(Next{});
     } else {
       wait_loads(Zero{});
     }
-    block(k1, sV1[wave], i + 1);
+    block(k1, kt1, sV1[wave], i + 1);
   }
 
   // Merge the waves' partial results for each query row.
