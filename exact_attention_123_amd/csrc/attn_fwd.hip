@@ -918,10 +918,13 @@ FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d) {
   return B * H * ((T + 255) / 256) < cus ? FwdPlan::kWaves4 : FwdPlan::kWaves8;
 }
 
-// K through LDS in the row-chunk forward (see attn_rows::row_chunk_attention)
-// for d = 64; at d = 128 the K stages would not fit LDS next to V's.
-template <int D>
-constexpr bool kRowsKLds = D == 64;
+// K through LDS in the row-chunk forward (see attn_rows::row_chunk_attention),
+// except at d = 128 with 8 waves, where the K stages would not fit LDS next
+// to V's.  Measured on MI355X (us per launch, K in LDS / in registers):
+// B H = 8, T = 2048, causal: d = 64 16.3 / 20.1, d = 128 29.8 / 37.4; no
+// mask, d = 64 19.0 / 24.9.
+template <int D, int NW>
+constexpr bool kRowsKLds = D == 64 || NW == 4;
 
 // Square forward on the row-chunk kernel: Tq = Tk = T, one key split (the
 // chunk's keys are cut only between its NW waves), O and LSE written
@@ -930,7 +933,7 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_fwd_rows_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int G, int NR, int nwg, float c) {
-  attn_rows::row_chunk_attention<D, CAUSAL, NW, kRowsKLds<D>>(Q, K, V, O, LSE, nullptr, nullptr, T,
+  attn_rows::row_chunk_attention<D, CAUSAL, NW, kRowsKLds<D, NW>>(Q, K, V, O, LSE, nullptr, nullptr, T,
                                                            T, T, G, 1, T, NR, nwg, c);
 }
 
