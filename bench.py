@@ -465,7 +465,7 @@ def main() -> int:
     else:
         do_bits = None
         # the instance attn_fwd launches for these sizes on this device
-        kname = (ea.kernel_name(True, d, causal) if dt == "f32"
+        kname = (ea.fwd_f32_kernel_name_for(B, H, T, d, causal) if dt == "f32"
                  else ea.fwd_kernel_name_for(B, H, T, d, causal))
         knames = [kname]
         fl = ea.flops(B, H, T, d, causal)
@@ -550,7 +550,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dt,
-        "data": "synthetic: seeded PCG64 N(0,1) draws rounded to bf16 (RNE)"
+        "data": ("synthetic: seeded PCG64 N(0,1) draws rounded to bf16 (RNE)" if dt == "bf16"
+                 else "synthetic: seeded PCG64 N(0,1) float32 draws")
                 + (", Q and K multiplied by 4" if w.get("qk_mult", 1.0) != 1.0 else "")
                 + ("; dO N(0,1) rounded to bf16" if bwd else ""),
         "config": config,

@@ -22,7 +22,7 @@ __all__ = [
     "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_fwd_gqa",
     "attn_bwd_gqa", "attn_decode", "decode", "decode_workspace_bytes", "decode_splits",
     "attn_fwd_materialized", "forward_materialized",
-    "kernel_name", "fwd_kernel_name_for",
+    "kernel_name", "fwd_kernel_name_for", "fwd_f32_kernel_name_for",
     "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
     "LIB_PATH", "STATUS", "flops", "bwd_flops",
 ]
@@ -56,6 +56,7 @@ EXPORTS = {
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_kernel_name": (ctypes.c_char_p, [ctypes.c_int, ctypes.c_int64, ctypes.c_int]),
     "attn_fwd_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
+    "attn_fwd_f32_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
 }
 
@@ -103,6 +104,13 @@ def fwd_kernel_name_for(B: int, H: int, T: int, d: int, causal: bool):
     """The bf16 forward instance attn_fwd launches for these sizes on the
     current device (needs a GPU)."""
     n = load_library().attn_fwd_kernel_name_for(B, H, T, d, int(bool(causal)))
+    return None if n is None else n.decode()
+
+
+def fwd_f32_kernel_name_for(B: int, H: int, T: int, d: int, causal: bool):
+    """The fp32 forward instance attn_fwd_f32 launches for these sizes on
+    the current device (needs a GPU)."""
+    n = load_library().attn_fwd_f32_kernel_name_for(B, H, T, d, int(bool(causal)))
     return None if n is None else n.decode()
 
 

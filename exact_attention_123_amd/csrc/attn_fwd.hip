@@ -824,6 +824,151 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// fp32 kernel for grids far smaller than the GPU (d = 64): one workgroup per
+// 32 query rows, the rows' visible keys split over the 4 waves in 32-key
+// blocks (wave w takes blocks w, w + 4, ...), the waves' partial results
+// merged in LDS with the online-softmax rescaling ("Attention Mechanism",
+// section 3).  The time of the 128-row kernel is one wave's chain of fp32
+// MFMAs over all keys of the longest query block; here it is a quarter of
+// that.  The problem is tiny, so each lane reads its K and V operands
+// straight from memory (bounded buffer loads: rows >= T read as zero), one
+// block ahead.
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_fwd_f32_rows_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, int G, float c) {
+  constexpr int D = 64, NDS = D / 2, NDT = D / 32, NW = kThreads / 64, BLK = 32;
+  __shared__ float sAcc[NW][32 * D];
+  __shared__ float sM[NW][32], sL[NW][32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 31, h = lane >> 5;
+  int bh, bhkv, qb;
+  block_coords(BH, nqb, G, bh, bhkv, qb);
+  const size_t head = (size_t)bh * (size_t)T * D;
+  const size_t kvhead = (size_t)bhkv * (size_t)T * D;
+  const int r0 = qb * 32;
+  const int qg = r0 + j;
+
+  // Q: B operand of S^T = K Q^T, lane (j, h) holds Q[qg][2 s + h].
+  float qf[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) qf[s] = qg < T ? Q[head + (size_t)qg * D + 2 * s + h] : 0.0f;
+
+  const int kv_end = CAUSAL ? min(T, r0 + 32) : T;
+  const int nblk = (kv_end + BLK - 1) / BLK;
+  const int nmine = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kvhead, T * D * 4);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kvhead, T * D * 4);
+
+  // Operands of block kb0: K[kb0 + j][2 s + h] (A of the score MFMA) and
+  // V[kb0 + acc_key_plain(r, h)][32 dt + j] (A of the P V MFMA).
+  auto load = [&](float (&kv)[NDS], float (&vv)[16 * NDT], int kb0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      kv[s] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rK, ((kb0 + j) * D + 2 * s + h) * 4, 0, 0));
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        vv[r * NDT + dt] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rV, ((kb0 + acc_key_plain(r, h)) * D + 32 * dt + j) * 4, 0, 0));
+  };
+
+  f32x16_t oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  auto block = [&](const float (&kv)[NDS], const float (&vv)[16 * NDT], int kb0)
+      __attribute__((always_inline)) {
+    f32x16_t x[1] = {f32x16_t{}};
+#pragma unroll
+    for (int s = 0; s < NDS; ++s)
+      x[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[s], qf[s], x[0], 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[0][r] *= c;
+    if (kb0 + BLK > T || (CAUSAL && kb0 + BLK - 1 > r0)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb0 + acc_key_plain(r, h);
+        if (key >= T || (CAUSAL && key > qg)) x[0][r] = -INFINITY;
+      }
+    }
+    float unused = 0.0f;  // fp32 P is not rounded: one normaliser serves O and LSE
+    online_softmax_update<1, NDT>(x, 1.0f, m_run, l_run, unused, oacc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) l_run += x[0][r];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r * NDT + dt], x[0][r], oacc[dt], 0,
+                                                        0, 0);
+  };
+
+  float k0[NDS], k1[NDS], v0[16 * NDT], v1[16 * NDT];
+  if (nmine > 0) load(k0, v0, BLK * wave);
+  for (int i = 0; i < nmine; i += 2) {
+    if (i + 1 < nmine) load(k1, v1, BLK * (wave + NW * (i + 1)));
+    block(k0, v0, BLK * (wave + NW * i));
+    if (i + 1 >= nmine) break;
+    if (i + 2 < nmine) load(k0, v0, BLK * (wave + NW * (i + 2)));
+    block(k1, v1, BLK * (wave + NW * (i + 1)));
+  }
+
+  // Merge the waves' partial results per query row: each wave's
+  // accumulator (relative to its own running max) into LDS, then 8 threads
+  // per row combine them.
+  l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4_t w;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = oacc[dt][4 * g + u];
+      *reinterpret_cast<f32x4_t*>(&sAcc[wave][j * D + 32 * dt + 8 * g + 4 * h]) = w;
+    }
+  if (h == 0) {
+    sM[wave][j] = m_run;
+    sL[wave][j] = l_run;
+  }
+  __syncthreads();
+  constexpr int CPT = D / 8;
+  const int row = tid >> 3, c0 = (tid & 7) * CPT;
+  const int q = r0 + row;
+  if (q >= T) return;
+  float M = sM[0][row];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sM[w][row]);
+  float a[NW], Lt = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    a[w] = sM[w][row] == -INFINITY ? 0.0f : exp2_hw(sM[w][row] - M);
+    Lt += a[w] * sL[w][row];
+  }
+  const float inv = 1.0f / Lt;
+  float* orow = O + head + (size_t)q * D + c0;
+#pragma unroll
+  for (int u = 0; u < CPT; u += 4) {
+    f32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) acc = fmaf(a[ww], sAcc[ww][row * D + c0 + u + e], acc);
+      w[e] = acc * inv;
+    }
+    *reinterpret_cast<f32x4_t*>(orow + u) = w;
+  }
+  if (c0 == 0) LSE[(size_t)bh * T + q] = (M + log2_hw(Lt)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
 // Host side: validation, device check, launch.
 // ---------------------------------------------------------------------------
 
@@ -916,6 +1061,19 @@ FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d) {
   }
   if (B * H * ((T + 127) / 128) * (d / 64) <= cus) return FwdPlan::kRows;
   return B * H * ((T + 255) / 256) < cus ? FwdPlan::kWaves4 : FwdPlan::kWaves8;
+}
+
+// The fp32 forward takes the row-chunk kernel (32 rows per workgroup, keys
+// split over 4 waves) at d = 64 when its 128-row grid has fewer workgroups
+// than the device has CUs.
+bool f32_rows(int64_t B, int64_t H, int64_t T, int64_t d) {
+  int dev = 0;
+  int64_t cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    const int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) cus = n;
+  }
+  return d == 64 && B * H * ((T + kBR - 1) / kBR) < cus;
 }
 
 // K through LDS in the row-chunk forward (see attn_rows::row_chunk_attention),
@@ -1040,6 +1198,10 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v, float* 
   attn_status st = validate(q, k, v, o, lse, B, H, H, T, d, causal, scale, 4, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
+  if (f32_rows(B, H, T, d))
+    return launch<float>(causal ? (const void*)attn_fwd_f32_rows_kernel<true>
+                                : (const void*)attn_fwd_f32_rows_kernel<false>,
+                         kThreads, 32, q, k, v, o, lse, B, H, H, T, scale, stream);
   return launch<float>(f32_kernel(d, causal), kThreads, kBR, q, k, v, o, lse, B, H, H, T, scale,
                        stream);
 }
@@ -1079,6 +1241,17 @@ const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d,
         "attn_fwd_rows_bf16_d128_causal_br32_bc32_w8"}}};
   if (plan == FwdPlan::kRows) return rows[rows_waves(T) == 8 ? 1 : 0][d == 128 ? 1 : 0][causal];
   return w4[d == 128 ? 1 : 0][causal];
+}
+
+const char* attn_fwd_f32_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d,
+                                         int causal) {
+  if (B <= 0 || H <= 0 || T <= 0 || (d != 64 && d != 128) || (causal != 0 && causal != 1))
+    return nullptr;
+  if (B > (int64_t(1) << 31) / H || T > (int64_t(1) << 31)) return nullptr;
+  if (check_device() != ATTN_OK) return nullptr;
+  if (!f32_rows(B, H, T, d)) return attn_kernel_name(1, d, causal);
+  return causal ? "attn_fwd_f32_rows_d64_causal_br32_bc32_w4"
+                : "attn_fwd_f32_rows_d64_full_br32_bc32_w4";
 }
 
 const char* attn_kernel_name(int is_f32, int64_t d, int causal) {

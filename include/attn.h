@@ -260,6 +260,17 @@ const char* attn_kernel_name(int is_f32, int64_t d, int causal);
 const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T,
                                      int64_t d, int causal);
 
+/*
+ * Name of the kernel instance attn_fwd_f32 launches for these sizes on the
+ * current device: at d = 64, when B * H * ceil(T / 128) is below the
+ * device's CU count, the row-chunk kernel (32 query rows per workgroup,
+ * their keys split over 4 waves, "attn_fwd_f32_rows_d64_causal_br32_bc32_w4"
+ * or "..._full_..."); otherwise the instance attn_kernel_name(1, d, causal)
+ * names.  NULL if the sizes are unsupported or the device is not a gfx950.
+ */
+const char* attn_fwd_f32_kernel_name_for(int64_t B, int64_t H, int64_t T,
+                                         int64_t d, int causal);
+
 #ifdef __cplusplus
 }
 #endif

@@ -127,6 +127,37 @@ def test_row_chunk_eight_waves(B, H, T, d, causal):
     assert eo <= to and el <= tl, (eo, el)
 
 
+# fp32: small grids at d = 64 run the fp32 row-chunk kernel (the ragged
+# shapes above); here the 128-row fp32 kernel on a grid that fills the GPU,
+# and the instance choice.
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_f32_large_grid(causal):
+    import exact_attention_123_amd as ea
+    B, H, T, d = 2, 64, 1000, 64
+    name = ea.fwd_f32_kernel_name_for(B, H, T, d, causal)
+    say(f"f32 large grid B={B} H={H} T={T} d={d} causal={causal}: {name}")
+    assert name == ea.kernel_name(True, d, causal)
+    seed = 1900 + int(causal)
+    x = make_qkv(B, H, T, d, dtype="f32", seed=seed)
+    scale = 1.0 / math.sqrt(d)
+    O, L = run(x, causal, scale)
+    eo, el = compare(x, O, L, causal, scale,
+                     rows_for=lambda b, h: boundary_rows(T, 16, seed + 31 * b + h),
+                     full_heads={(0, 0)})
+    to, tl = TOL["f32"]
+    assert eo <= to and el <= tl, (eo, el)
+
+
+def test_f32_instance_choice():
+    import exact_attention_123_amd as ea
+    assert (ea.fwd_f32_kernel_name_for(1, 1, 256, 64, True)
+            == "attn_fwd_f32_rows_d64_causal_br32_bc32_w4")
+    assert (ea.fwd_f32_kernel_name_for(1, 1, 256, 64, False)
+            == "attn_fwd_f32_rows_d64_full_br32_bc32_w4")
+    assert ea.fwd_f32_kernel_name_for(1, 1, 256, 128, True) == ea.kernel_name(True, 128, True)
+    assert ea.fwd_f32_kernel_name_for(0, 1, 256, 64, True) is None
+
+
 def test_small_grid_uses_row_chunks():
     """Problems too small to fill the GPU with 256-row workgroups take the
     row-chunk kernel when the 4-wave grid (in d = 64 units) fits the CUs
