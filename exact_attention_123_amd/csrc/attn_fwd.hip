@@ -1046,9 +1046,9 @@ attn_status check_device() {
 //    grid has fewer workgroups than the device has CUs;
 //  - else the 8-wave kernel.
 // Measured on MI355X (average launch, bf16): the row-chunk kernel takes
-// 20 us against 37 us (4-wave) at B H = 8, T = 2048, d = 64, causal, 217
-// against 282 us at B H = 1, T = 16384, d = 128, causal, and 157 against
-// 83 us at B H = 8, T = 4096, d = 128, no mask, where the 4-wave grid
+// 16 us against 37 us (4-wave) at B H = 8, T = 2048, d = 64, causal, 167
+// against 282 us at B H = 1, T = 16384, d = 128, causal, but 112 against
+// 83 us at B H = 8, T = 4096, d = 128, causal, where the 4-wave grid
 // already fills the CUs twice in d = 64 units.
 enum class FwdPlan { kWaves8, kWaves4, kRows };
 
@@ -1091,8 +1091,8 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_fwd_rows_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int G, int NR, int nwg, float c) {
-  attn_rows::row_chunk_attention<D, CAUSAL, NW, kRowsKLds<D, NW>>(Q, K, V, O, LSE, nullptr, nullptr, T,
-                                                           T, T, G, 1, T, NR, nwg, c);
+  attn_rows::row_chunk_attention<D, CAUSAL, NW, kRowsKLds<D, NW>>(
+      Q, K, V, O, LSE, nullptr, nullptr, T, T, T, G, 1, T, NR, nwg, c);
 }
 
 template <int NW>
@@ -1104,13 +1104,14 @@ const void* rows_kernel(int64_t d, int causal) {
 }
 
 // Waves of the row-chunk kernel: 4, or 8 for sequences of at least 4096
-// keys.  The kernel's time is mostly the chunks re-reading their keys from
-// L2, which more waves do not change; only long key ranges gain from the
-// shorter per-wave chain.  Measured on MI355X (us per launch, 8 / 4
-// waves): B H = 1, T = 16384, d = 128, causal 167 / 217; B H = 4, T = 4096,
+// keys.  More waves shorten each wave's chain of key blocks, but fewer
+// workgroups then fit a CU (registers, LDS); only long key ranges gain.
+// Measured on MI355X with K in registers (us per launch, 8 / 4 waves):
+// B H = 1, T = 16384, d = 128, causal 167 / 217; B H = 4, T = 4096,
 // d = 128, causal 55 / 61; B H = 8, T = 4096, d = 64, causal 56 / 56; but
 // B H = 8, T = 2048, d = 64, causal 24 / 20 and B H = 16, T = 1024,
-// d = 128, no mask 35 / 28.
+// d = 128, no mask 35 / 28 (with K in LDS at d = 64, 8 waves for every
+// length: 18.2 against 16.3 us at T = 2048).
 int rows_waves(int64_t T) { return T >= 4096 ? 8 : 4; }
 
 attn_status launch_rows(int64_t d, int causal, const void* q, const void* k, const void* v,

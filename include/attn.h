@@ -32,9 +32,9 @@
  *
  * Ownership.  The caller owns every buffer.  The library allocates, frees
  * and keeps no device memory; the forward uses no workspace, the backward,
- * the decode and the materialised forward caller-owned ones.  It holds no mutable state other than a per-device
- * cache of the architecture check, and may be called from several host
- * threads.
+ * the decode and the materialised forward caller-owned ones.  It holds no
+ * mutable state other than a per-device cache of the architecture check
+ * and CU count, and may be called from several host threads.
  *
  * Asynchrony.  Calls enqueue their kernels (one for the forward, three for
  * the backward and the materialised forward, one or two for the decode) on
