@@ -52,7 +52,6 @@ using attn_rows::kMaxRows;
 using attn_rows::kThreads;
 using attn_rows::kWaves;
 
-constexpr int kMaxChunks = 8;  // Tq * G <= 256 query rows per key/value head
 // Key split: about kTargetGroups workgroups (one round at two per CU), each
 // split at least kMinSplitKeys long: short splits cost a prologue, an LDS
 // merge and partial results each (measured: 32 splits of 4096 keys read a
@@ -154,12 +153,15 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
   // the new queries are the last Tq positions of the cache; a query needs at
   // least one key
   if (Tk < 1 || (causal && Tk < Tq)) return ATTN_ERR_SHAPE;
-  if (Tq * (H / H_kv) > kMaxRows * kMaxChunks) return ATTN_ERR_UNSUPPORTED;
+  // row and grid indices are 32-bit: Tq G rows per key/value head, their
+  // 32-row chunks over all heads, B H Tq output rows
+  if (Tq * (H / H_kv) > (int64_t(1) << 30)) return ATTN_ERR_SHAPE;
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if ((Tk_cap + 64) * d * 2 > kMaxHeadBytes) return ATTN_ERR_SHAPE;
   if (B > (int64_t(1) << 31) / H) return ATTN_ERR_SHAPE;
   if (B * H > (INT64_MAX / 8) / (Tk_cap * d * 2)) return ATTN_ERR_SHAPE;
-  if (B * H_kv * kTargetGroups * kMaxChunks > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (B * H_kv * row_chunks(Tq, H / H_kv) > (int64_t(1) << 30)) return ATTN_ERR_SHAPE;
+  if (B * H * Tq > INT32_MAX) return ATTN_ERR_SHAPE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return ATTN_ERR_ALIGN;
   if ((uintptr_t)lse & 3u) return ATTN_ERR_ALIGN;
   const int64_t qb = B * H * Tq * d * 2, kb = B * H_kv * Tk_cap * d * 2, lb = B * H * Tq * 4;

@@ -177,11 +177,13 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
  *   k, v:  const __hip_bfloat16 caches [B][H_kv][Tk_cap][d] of which rows
  *          0 .. Tk-1 of each head are valid (rows >= Tk are never read);
  *   H_kv divides H, query head h reads key/value head h / (H / H_kv);
- *   Tq * (H / H_kv) <= 256 (more new queries per key/value head are a
- *          prefill: ATTN_ERR_UNSUPPORTED); up to 32 of them share one
- *          workgroup and one read of the keys, more take one workgroup per
- *          32 rows;  1 <= Tk <= Tk_cap, and Tk >= Tq when causal
- *          (ATTN_ERR_SHAPE otherwise);
+ *   Tq * (H / H_kv) query rows per key/value head, at most 2^30: up to
+ *          32 of them share one workgroup and one read of the keys, more
+ *          take one workgroup per 32 rows (many new queries appended to a
+ *          cache, a prefill in chunks, run the same way; under the causal
+ *          mask a workgroup reads only the keys its rows can see);
+ *          1 <= Tk <= Tk_cap, and Tk >= Tq when causal (ATTN_ERR_SHAPE
+ *          otherwise);
  *   ws, ws_bytes: caller-owned device workspace of at least
  *          attn_decode_workspace_bytes(B, H, H_kv, Tq, Tk, d) bytes,
  *          16-byte aligned (may be NULL when that is 0), overwritten.  Too

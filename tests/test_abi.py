@@ -196,7 +196,7 @@ def test_decode_validation_errors():
     assert dec(Tk=0) == 2                  # a query needs a key
     assert dec(Tq=3, Tk=2, Tcap=2) == 2    # causal: the queries are cache positions
     assert dec(Tcap=50) == 2               # valid length beyond capacity
-    assert dec(Tq=65) == 3                 # 65 * 4 rows > 256 per key/value head
+    assert dec(Tq=1 << 29, Tk=1 << 29, Tcap=1 << 29) == 2  # 2^31 rows per key/value head
     assert dec(d=96) == 3
     assert dec(q=0) == 1
     assert dec(causal=2) == 6
@@ -210,6 +210,16 @@ def test_decode_validation_errors():
     assert dec(ws=6 << 36, wsb=16, **far) == 9
 
 
+@no_gpu_only
+def test_decode_many_query_rows_pass_validation():
+    # 4096 new queries x 4 query heads per key/value head: a prefill in
+    # chunks; validation accepts it and only the device check (no GPU) stops
+    # it
+    r = ea.attn_decode(1 << 36, 2 << 36, 3 << 36, 4 << 36, 5 << 36, 6 << 36, 1 << 30, 1, 8, 2,
+                       4096, 8192, 8192, 128, 1, 0.1)
+    assert r == 7
+
+
 def test_decode_split_sizes():
     # about 512 workgroups, each split at least 4096 keys
     assert ea.decode_splits(1, 32, 8, 1, 131072) == 32
@@ -221,6 +231,9 @@ def test_decode_split_sizes():
     assert ea.decode_splits(1, 32, 8, 1, 262144) == 64
     assert ea.decode_splits(1, 32, 8, 16, 262144) == 32
     assert ea.decode_workspace_bytes(2048, 32, 8, 1, 4096, 128) == 0
+    # a prefill in chunks: 512 row chunks over the two key/value heads, one split
+    assert ea.decode_splits(1, 8, 2, 2048, 8192) == 1
+    assert ea.decode_workspace_bytes(1, 8, 2, 2048, 8192, 128) == 0
     assert ea.decode_workspace_bytes(1, 32, 8, 1, 131072, 128) == 32 * 32 * 129 * 4
 
 

@@ -5,9 +5,10 @@ Tolerances as for the bf16 forward: max abs error 2e-2 on O and 1e-3 on LSE.
 Cache rows past the valid length hold NaN bit patterns, so any read beyond
 Tk shows up as a non-finite output.  Shapes cover one and several new
 queries, grouped key/value heads (G = 1, 4, 8), more query rows per
-key/value head than one workgroup takes (up to the 256-row limit), caches
-shorter than one block, ragged lengths, a single split and many splits (the
-cross-split merge), and the full decode workloads on sampled heads.
+key/value head than one workgroup takes (256 rows, and thousands: a prefill
+in chunks appended to a cache), caches shorter than one block, ragged
+lengths, a single split and many splits (the cross-split merge), and the
+full decode workloads on sampled heads.
 """
 import math
 import sys
@@ -73,6 +74,20 @@ def test_decode_shapes(Tq, H, Hkv, Tk, causal, d):
     scale = 1.0 / math.sqrt(d)
     x = make_decode(B, H, Hkv, Tq, Tk, d, seed=9000 + Tq + H + Hkv + Tk + d, Tk_cap=Tk + 37,
                     qk_mult=2.0)
+    O, L = run_decode(x, causal, scale, Tk)
+    check(x, O, L, causal, scale, Tk)
+
+
+# Many new queries appended to a cache (a prefill in chunks): row chunks
+# by the hundred, each reading only the keys its rows see under the causal
+# mask; Tq = Tk is the square forward.
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("B,H,Hkv,Tq,Tk,d", [(1, 8, 2, 300, 1500, 128), (1, 4, 4, 1000, 1000, 64),
+                                            (2, 2, 1, 777, 2049, 64)])
+def test_decode_chunked_prefill(B, H, Hkv, Tq, Tk, d, causal):
+    say(f"[decode prefill chunk] B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d} causal={causal}")
+    scale = 1.0 / math.sqrt(d)
+    x = make_decode(B, H, Hkv, Tq, Tk, d, seed=9500 + Tq + Tk + d, Tk_cap=Tk + 5, qk_mult=2.0)
     O, L = run_decode(x, causal, scale, Tk)
     check(x, O, L, causal, scale, Tk)
 
