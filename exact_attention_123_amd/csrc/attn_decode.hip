@@ -41,6 +41,7 @@
 #include <cstring>
 
 #include "attn.h"
+#include "fwd_cache.h"
 #include "rows.h"
 #include "tiles.h"
 
@@ -119,6 +120,20 @@ attn_status check_device() {
 // Workgroups per (key/value head, split): one per 32 query rows.
 int64_t row_chunks(int64_t Tq, int64_t G) { return (Tq * G + kMaxRows - 1) / kMaxRows; }
 
+// With many query rows per key/value head the work is the contractions,
+// not reading the cache; when in addition the forward kernel's grid (of
+// 128-row workgroups) fills the device, that kernel (software pipelined, K and V tiles shared by its
+// 8 or 4 waves) runs them over the cache instead of the row-chunk kernel.
+// Measured on MI355X (us, forward / row-chunk): B = 2, 16 heads, Tq =
+// 1024, Tk = 4096, d = 128 91 / 145; but 32 query / 8 key-value heads,
+// Tq = 64, Tk = 8192 143 / 44 and 8 heads, Tq = 2048, Tk = 16384, d = 64
+// 208 / 142 (grids below one 128-row workgroup per CU).
+constexpr int64_t kFwdMinRows = 256;
+bool over_forward(int64_t B, int64_t H, int64_t H_kv, int64_t Tq) {
+  return Tq * (H / H_kv) >= kFwdMinRows && attn_internal::fwd_fills_device(B, H, Tq);
+}
+
+
 // Split of the keys: about kTargetGroups workgroups over the B*H_kv groups
 // (times their row chunks),
 // each split at least kMinSplitKeys keys (fewer splits when the cache is
@@ -134,6 +149,15 @@ int64_t choose_split(int64_t BHkv, int64_t Tk, int64_t* kps) {
   per = (per + unit - 1) / unit * unit;
   *kps = per;
   return (Tk + per - 1) / per;
+}
+
+// Key splits of a call (one when the forward kernel runs it).
+int64_t splits_for(int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk, int64_t* kps) {
+  if (over_forward(B, H, H_kv, Tq)) {
+    *kps = Tk;
+    return 1;
+  }
+  return choose_split(B * H_kv * row_chunks(Tq, H / H_kv), Tk, kps);
 }
 
 attn_status validate(const void* q, const void* k, const void* v, const void* o,
@@ -187,7 +211,7 @@ int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t 
   if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || (d != 64 && d != 128)) return 0;
   if (H % H_kv != 0) return 0;
   int64_t kps;
-  const int64_t n = choose_split(B * H_kv * row_chunks(Tq, H / H_kv), Tk, &kps);
+  const int64_t n = splits_for(B, H, H_kv, Tq, Tk, &kps);
   return n > 1 ? n * B * H * Tq * (d + 1) * 4 : 0;
 }
 
@@ -201,7 +225,7 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
   if (st != ATTN_OK || empty) return st;
   int64_t kps;
   const int64_t nchunk = row_chunks(Tq, H / H_kv);
-  const int64_t nsplit = choose_split(B * H_kv * nchunk, Tk, &kps);
+  const int64_t nsplit = splits_for(B, H, H_kv, Tq, Tk, &kps);
   const int64_t NR = B * H * Tq;
   const int64_t need = nsplit > 1 ? nsplit * NR * (d + 1) * 4 : 0;
   float* part_o = nullptr;
@@ -217,6 +241,9 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
     part_lse = part_o + nsplit * NR * d;
   }
   if ((st = check_device()) != ATTN_OK) return st;
+  if (over_forward(B, H, H_kv, Tq))
+    return attn_internal::fwd_over_cache(q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap, d, causal,
+                                         scale, stream);
 
   int tq = (int)Tq, tk = (int)Tk, tcap = (int)Tk_cap, g = (int)(H / H_kv), ns = (int)nsplit,
       kp = (int)kps, nr = (int)NR, nwg = (int)(B * H_kv * nsplit);
@@ -244,7 +271,7 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
 int64_t attn_decode_splits(int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk) {
   if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || H % H_kv != 0) return 0;
   int64_t kps;
-  return choose_split(B * H_kv * row_chunks(Tq, H / H_kv), Tk, &kps);
+  return splits_for(B, H, H_kv, Tq, Tk, &kps);
 }
 
 }  // extern "C"

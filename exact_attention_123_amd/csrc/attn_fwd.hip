@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "fwd_cache.h"
 #include "rows.h"
 #include "tiles.h"
 
@@ -272,7 +273,8 @@ __device__ __forceinline__ float sum_tree(const float* x) {
 template <int D, bool CAUSAL, bool PRESCALE, int NWAVES>
 __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int T, int BH, int nqb, int G, float c) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int T, int Tk, int Tcap, int off, int BH, int nqb, int G,
+    float c) {
   using C = Bf16Tile<D, NWAVES>;
   constexpr int BR = 32 * NWAVES;  // query rows per workgroup
   constexpr int NW = C::NW, BC = C::BC, NDS = C::NDS, NDT = C::NDT;
@@ -295,8 +297,12 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   const int j = lane & 31, h = lane >> 5;
   int bh, bhkv, qb;
   block_coords(BH, nqb, G, bh, bhkv, qb);
+  // T query rows per head (Q, O, LSE); Tk keys per key/value head, stored
+  // with a row stride of Tcap rows per head; query row i sits at key
+  // position i + off (off = 0 for the square forward, Tk - T for new
+  // queries appended to a cache).
   const size_t head = (size_t)bh * (size_t)T * D;
-  const size_t kvhead = (size_t)bhkv * (size_t)T * D;
+  const size_t kvhead = (size_t)bhkv * (size_t)Tcap * D;
   const int head_bytes = T * RB;
   const __bf16* Kh = K + kvhead;
   const __bf16* Vh = V + kvhead;
@@ -308,10 +314,11 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   const int rg = NW == 8 && wave >= 4 ? 11 - wave : wave;
   const int qg = q0 + rg * 32 + j;
   // Under a causal mask the last score sub-tile (32 keys) with a key visible
-  // to some row of the wave is klast = q0 / 32 + rg; from iteration tskip on
+  // to some row of the wave is klast = (off + q0 + 32 rg + 31) / 32 (for
+  // the square forward q0 / 32 + rg); from iteration tskip on
   // (sub-steps k >= 2 tskip + 1 > klast + 1: nothing left to accumulate)
   // the wave only loads its share of the tiles and joins the barriers.
-  const int tskip = CAUSAL ? (q0 / 32 + rg) / 2 + 1 : INT32_MAX;
+  const int tskip = CAUSAL ? ((off + q0 + 32 * rg + 31) / 32) / 2 + 1 : INT32_MAX;
 
   // Q fragment: B operand of S^T = K Q^T; lane (j, h) holds
   // Q[qg][16 s + 8 h .. +8] for every k-step s.  Rows >= T read as zero.
@@ -323,12 +330,12 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
       qf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rQ, qg * RB + (16 * s + 8 * h) * 2));
   }
 
-  const int kv_end = CAUSAL ? min(T, q0 + BR) : T;
+  const int kv_end = CAUSAL ? min(Tk, off + q0 + BR) : Tk;
   const int ntiles = (kv_end + BC - 1) / BC;
   const int kv_bytes = kv_end * RB;
-  // Score sub-tiles (32 keys) below nfs need no mask: every key is < T and,
-  // when causal, no later than the workgroup's first query.
-  const int nfs = (CAUSAL ? min(q0 + 1, T) : T) / 32;
+  // Score sub-tiles (32 keys) below nfs need no mask: every key is < Tk
+  // and, when causal, no later than the workgroup's first query.
+  const int nfs = (CAUSAL ? min(off + q0 + 1, Tk) : Tk) / 32;
 
   // Direct-to-LDS loads.  A 1 KiB block is written by one wave instruction,
   // lane L's 16 bytes landing at block offset 16 L; each lane picks the
@@ -578,7 +585,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 32 * k + acc_key_perm(r, h);
-      if (key >= T || (CAUSAL && key > qg)) x[r] = -INFINITY;
+      if (key >= Tk || (CAUSAL && key > qg + off)) x[r] = -INFINITY;
     }
   };
 
@@ -1159,6 +1166,26 @@ const void* bf16_kernel(int64_t d, int causal, float scale, int nw) {
   return scale > 0.0f ? bf16_kernel_p<false, 8>(d, causal) : bf16_kernel_p<true, 8>(d, causal);
 }
 
+// Launches the bf16 kernel with `nw` waves (32 nw query rows per
+// workgroup) over T query rows per head and Tk keys per key/value head
+// stored with a stride of Tcap rows; query row i sits at key position
+// i + off.
+attn_status launch_bf16(int nw, int64_t d, int causal, float scale, const void* q, const void* k,
+                        const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Hkv,
+                        int64_t T, int64_t Tk, int64_t Tcap, int64_t off, hipStream_t stream) {
+  const void* kernel = bf16_kernel(d, causal, scale, nw);
+  const int rows = 32 * nw;
+  int t = (int)T, tk = (int)Tk, tcap = (int)Tcap, of = (int)off, bh = (int)(B * H),
+      nqb = (int)((T + rows - 1) / rows), g = (int)(H / Hkv);
+  float c = scale * kLog2e;
+  void* args[] = {(void*)&q,  (void*)&k,   (void*)&v,  (void*)&o,   (void*)&lse,
+                  (void*)&t,  (void*)&tk,  (void*)&tcap, (void*)&of, (void*)&bh,
+                  (void*)&nqb, (void*)&g,  (void*)&c};
+  const dim3 grid((unsigned)(bh * nqb)), block(64 * nw);
+  if (hipLaunchKernel(kernel, grid, block, args, 0, stream) != hipSuccess) return ATTN_ERR_LAUNCH;
+  return ATTN_OK;
+}
+
 const void* f32_kernel(int64_t d, int causal) {
   if (d == 64) return causal ? (const void*)attn_fwd_f32_kernel<64, true>
                              : (const void*)attn_fwd_f32_kernel<64, false>;
@@ -1167,6 +1194,31 @@ const void* f32_kernel(int64_t d, int causal) {
 }
 
 }  // namespace
+
+namespace attn_internal {
+
+bool fwd_fills_device(int64_t B, int64_t H, int64_t Tq) {
+  check_device();  // caches the CU count (256 assumed without a device)
+  int dev = 0;
+  int64_t cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+    const int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) cus = n;
+  }
+  return B * H * ((Tq + 127) / 128) >= cus;
+}
+
+attn_status fwd_over_cache(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                           int64_t Tk_cap, int64_t d, int causal, float scale,
+                           hipStream_t stream) {
+  if (check_device() != ATTN_OK) return ATTN_ERR_DEVICE;
+  const int nw = pick_plan(B, H, Tq, d) == FwdPlan::kWaves8 ? 8 : 4;
+  return launch_bf16(nw, d, causal, scale, q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap,
+                     causal ? Tk - Tq : 0, stream);
+}
+
+}  // namespace attn_internal
 
 extern "C" {
 
@@ -1181,9 +1233,7 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   if (plan == FwdPlan::kRows)
     return launch_rows(d, causal, q, k, v, o, lse, B, H, H_kv, T, scale, stream);
   const int nw = plan == FwdPlan::kWaves4 ? 4 : 8;
-  return launch<__bf16>(bf16_kernel(d, causal, scale, nw), 64 * nw, 32 * nw, (const __bf16*)q,
-                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, B, H, H_kv, T,
-                        scale, stream);
+  return launch_bf16(nw, d, causal, scale, q, k, v, o, lse, B, H, H_kv, T, T, T, 0, stream);
 }
 
 attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,

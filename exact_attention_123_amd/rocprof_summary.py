@@ -57,10 +57,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 _CSRC = os.path.join(PKG, "csrc")
 # the kernel code of each pass: its source and the headers it includes
 SOURCES = {"fwd": [os.path.join(_CSRC, "attn_fwd.hip"), os.path.join(_CSRC, "rows.h"),
-                   os.path.join(_CSRC, "tiles.h")],
+                   os.path.join(_CSRC, "tiles.h"), os.path.join(_CSRC, "fwd_cache.h")],
            "bwd": [os.path.join(_CSRC, "attn_bwd.hip"), os.path.join(_CSRC, "tiles.h")],
            "decode": [os.path.join(_CSRC, "attn_decode.hip"), os.path.join(_CSRC, "rows.h"),
-                      os.path.join(_CSRC, "tiles.h")],
+                      os.path.join(_CSRC, "tiles.h"), os.path.join(_CSRC, "fwd_cache.h")],
            "mat": [os.path.join(_CSRC, "attn_materialized.hip"), os.path.join(_CSRC, "tiles.h")]}
 # substring of the pass's kernel symbols
 MARKS = {"fwd": "attn_fwd_", "bwd": "attn_bwd_", "decode": "attn_decode_", "mat": "attn_mat_"}

@@ -181,7 +181,10 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
  *          32 of them share one workgroup and one read of the keys, more
  *          take one workgroup per 32 rows (many new queries appended to a
  *          cache, a prefill in chunks, run the same way; under the causal
- *          mask a workgroup reads only the keys its rows can see);
+ *          mask a workgroup reads only the keys its rows can see; with
+ *          at least 256 of them and B * H * ceil(Tq / 128) at least the
+ *          device's CU count, the forward kernel runs them instead, as one
+ *          kernel with no workspace);
  *          1 <= Tk <= Tk_cap, and Tk >= Tq when causal (ATTN_ERR_SHAPE
  *          otherwise);
  *   ws, ws_bytes: caller-owned device workspace of at least

@@ -92,6 +92,28 @@ def test_decode_chunked_prefill(B, H, Hkv, Tq, Tk, d, causal):
     check(x, O, L, causal, scale, Tk)
 
 
+# Many new queries on a grid of at least one 128-row workgroup per CU:
+# the forward kernel runs them over the cache (query i at key position
+# Tk - Tq + i); sampled heads against the oracle.
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("B,H,Hkv,Tq,Tk,d", [(2, 32, 8, 520, 1700, 128), (4, 32, 8, 300, 900, 64),
+                                            (1, 64, 64, 513, 513, 128)])
+def test_decode_over_forward_kernel(B, H, Hkv, Tq, Tk, d, causal):
+    import exact_attention_123_amd as ea
+    say(f"[decode on the forward kernel] B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d} "
+        f"causal={causal}")
+    assert B * H * ((Tq + 127) // 128) >= 256 and Tq * (H // Hkv) >= 256
+    assert ea.decode_splits(B, H, Hkv, Tq, Tk) == 1
+    assert ea.decode_workspace_bytes(B, H, Hkv, Tq, Tk, d) == 0
+    scale = 1.0 / math.sqrt(d)
+    x = make_decode(B, H, Hkv, Tq, Tk, d, seed=9600 + Tq + Tk + d, Tk_cap=Tk + 9, qk_mult=2.0)
+    O, L = run_decode(x, causal, scale, Tk)
+    heads = [(0, 0), (0, H - 1), (B - 1, H // 2), (B - 1, 1)]
+    check(x, O, L, causal, scale, Tk, heads=heads)
+    # every row finite (rows past the valid cache hold NaN bit patterns)
+    assert np.isfinite(O).all()
+
+
 @pytest.mark.parametrize("scale", [-0.25, 0.0, 1.0])
 def test_decode_other_scales(scale):
     say(f"[decode scale] {scale}")
