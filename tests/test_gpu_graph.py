@@ -1,6 +1,7 @@
 """HIP graph capture of the entry points: the forward (one kernel), the
-backward (three kernels and a workspace) and the decode path with several
-key splits (split kernel, merge kernel, workspace) are captured once into a
+backward (three kernels and a workspace) and the decode path (several key
+splits with a merge kernel and a workspace; a prefill chunk on the row-chunk
+kernel; a large chunk on the forward kernel over the cache) are captured into a
 torch.cuda.CUDAGraph and replayed several times.  Between replays the inputs
 are overwritten eagerly (host-to-device copies, then a synchronisation), and
 every replay's outputs must equal, bit for bit, an eager call on the same
@@ -100,23 +101,30 @@ def test_backward_graph_replays():
             assert torch.equal(got, want), rep
 
 
-def test_decode_graph_replays():
+# Three decode routes: several key splits (split kernel, merge kernel,
+# workspace); a prefill chunk of 600 rows per key/value head on the
+# row-chunk kernel (one split, no workspace); and a chunk large enough for
+# the forward kernel over the cache (key offset Tk - Tq).
+@pytest.mark.parametrize("B,H,Hkv,Tq,Tk,d", [(1, 8, 2, 2, 20000, 128), (1, 8, 2, 150, 3000, 64),
+                                            (2, 32, 8, 520, 1700, 128)],
+                         ids=["splits", "rows", "forward"])
+def test_decode_graph_replays(B, H, Hkv, Tq, Tk, d):
     import torch
 
     import exact_attention_123_amd as ea
-    say("[graph decode]")
-    B, H, Hkv, Tq, Tk, d = 1, 8, 2, 2, 20000, 128
-    assert ea.decode_splits(B, H, Hkv, Tq, Tk) > 1
-    x = make_decode(B, H, Hkv, Tq, Tk, d, seed=8300)
+    say(f"[graph decode] B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d}")
+    splits = ea.decode_splits(B, H, Hkv, Tq, Tk)
+    need = ea.decode_workspace_bytes(B, H, Hkv, Tq, Tk, d)
+    assert (splits > 1) == (need > 0) == (Tq == 2)
+    x = make_decode(B, H, Hkv, Tq, Tk, d, seed=8300 + Tq)
     q, kc, vc = (to_device(a, "bf16") for a in (x.q, x.k, x.v))
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
-    ws = torch.empty(ea.decode_workspace_bytes(B, H, Hkv, Tq, Tk, d), dtype=torch.uint8,
-                     device=q.device)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     scale = 1.0 / math.sqrt(d)
     g = capture(lambda: ea.decode(q, kc, vc, Tk=Tk, causal=True, scale=scale, out=o, lse=lse,
                                   ws=ws))
-    rng = np.random.Generator(np.random.PCG64(8301))
+    rng = np.random.Generator(np.random.PCG64(8301 + Tq))
     for rep in range(REPLAYS):
         q.copy_(fresh_bf16((B, H, Tq, d), rng, 2.0))
         torch.cuda.synchronize()
