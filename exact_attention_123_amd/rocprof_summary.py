@@ -37,9 +37,9 @@ name or the backward's dK/dV kernel name:
     python -m exact_attention_123_amd.rocprof_summary --pass fwd \
         --workload bf16_b1h32_t8192_d128_causal_qk4 --name <kernel> \
         --flops F --alg-bytes A \
-        --stats gpurun_out/kt/kt_kernel_stats.csv \
-        --fetch gpurun_out/pmc_fetch/f_counter_collection.csv \
-        --write gpurun_out/pmc_write/w_counter_collection.csv \
+        --stats prof/kt/kt_kernel_stats.csv \
+        --fetch prof/pmc_fetch/f_counter_collection.csv \
+        --write prof/pmc_write/w_counter_collection.csv \
         --copy-mib 1024 --kt-cmd '...' --fetch-cmd '...' --write-cmd '...'
 """
 from __future__ import annotations
