@@ -403,7 +403,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(heads shard across GPUs with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
