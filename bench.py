@@ -26,6 +26,15 @@ HBM-bound: the roofline is GB/s of the S and P traffic (plus Q, K, V, O, LSE)
 against 8 TB/s, and the fused forward is timed in the same run for the
 comparison.
 
+Timing: W untimed warm-up steps, then untimed steps until --settle-ms (default
+2 s) of wall time has passed since the warm-up began (the shader clock of a
+cold GPU needs a few hundred launches to reach its loaded steady state), then
+K steps between HIP events on the launch stream.  The record carries the
+settle phase's length, the first and last five launch durations, and the
+shader and memory clocks, socket power and power-limit residency sampled
+(amdsmi, host-side) over the settle phase's last 500 ms and over the timed
+region.
+
 Prints one JSON line with the throughput, the roofline position of the pass
 (MFMA-bound, against MI355X's dense bf16 peak; for the backward the three
 kernels of one call are timed together) and the float64 CPU oracle timed on a
@@ -119,17 +128,143 @@ def cpu_baseline(x, causal: bool, scale: float, heads: int, pass_: str, do_bits=
                   f"{dt:.1f} s wall",
         "seconds": dt,
         "host_cpus": len(os.sched_getaffinity(0)),
+        "blas": blas_info(),
     }
 
 
-def time_steps(step, stream, steps: int, warmup: int):
-    """W untimed steps, then K steps between HIP events on the launch
-    stream.  Returns (per-step ms list, region ms, wall s)."""
+class GpuMetricsSampler:
+    """Samples the GPU's clocks, power and throttle-residency counters
+    (amdsmi's gpu_metrics table, host-side reads only) on a background thread
+    while the benchmark runs, so that the record shows the clock state the
+    timed launches ran at.  Any failure (no amdsmi, no permission) leaves the
+    fields None with the reason."""
+
+    KEYS = ("current_gfxclks", "current_gfxclk", "current_uclk", "current_socket_power",
+            "energy_accumulator", "accumulation_counter", "ppt_residency_acc",
+            "socket_thm_residency_acc", "temperature_hotspot")
+
+    def __init__(self, period_s: float = 0.004):
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._handle = None
+        self._stop = None
+        self._thread = None
+
+    def start(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("no GPU handle")
+            self._handle = handles[0]
+            self._amdsmi = amdsmi
+            self._read()  # fail here rather than in the thread
+        except Exception as e:  # pragma: no cover - depends on the machine
+            self.error = f"{type(e).__name__}: {e}"
+            return self
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        return (time.perf_counter(), {k: m.get(k) for k in self.KEYS})
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append(self._read())
+            except Exception as e:  # pragma: no cover
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            try:
+                self.samples.append(self._read())
+                self._amdsmi.amdsmi_shut_down()
+            except Exception:  # pragma: no cover
+                pass
+
+    @staticmethod
+    def _num(v):
+        return v if isinstance(v, (int, float)) and v not in (65535, 0xFFFFFFFF) else None
+
+    def window(self, t0: float, t1: float):
+        """Summary of the samples taken in [t0, t1] (perf_counter seconds):
+        median shader clock over the XCDs, memory clock, socket power, and
+        from the accumulators the average power and the fraction of the
+        window spent at the package power limit."""
+        if self.error and not self.samples:
+            return {"error": self.error}
+        sel = [(t, m) for t, m in self.samples if t0 <= t <= t1]
+        if not sel:
+            return {"samples": 0}
+
+        def med(xs):
+            xs = sorted(x for x in xs if x is not None)
+            return xs[len(xs) // 2] if xs else None
+
+        def xcd_mean(m):
+            v = m.get("current_gfxclks")
+            vals = [self._num(x) for x in v] if isinstance(v, (list, tuple)) else []
+            vals = [x for x in vals if x]
+            return sum(vals) / len(vals) if vals else self._num(m.get("current_gfxclk"))
+
+        out = {"samples": len(sel),
+               "sclk_mhz_median": med([xcd_mean(m) for _, m in sel]),
+               "sclk_mhz_min": min((x for x in (xcd_mean(m) for _, m in sel) if x),
+                                   default=None),
+               "mclk_mhz_median": med([self._num(m.get("current_uclk")) for _, m in sel]),
+               "socket_power_w_median": med([self._num(m.get("current_socket_power"))
+                                             for _, m in sel]),
+               "hotspot_c_max": max((self._num(m.get("temperature_hotspot")) or 0
+                                     for _, m in sel), default=None)}
+        (ta, a), (tb, b) = sel[0], sel[-1]
+        try:
+            de = b["energy_accumulator"] - a["energy_accumulator"]
+            if tb > ta and de >= 0:
+                # the accumulator counts 15.259 uJ (2^-16 J) units
+                out["avg_power_w_from_energy"] = round(de * 15.259e-6 / (tb - ta), 1)
+            dacc = b["accumulation_counter"] - a["accumulation_counter"]
+            if dacc > 0:
+                out["ppt_limited_frac"] = round(
+                    (b["ppt_residency_acc"] - a["ppt_residency_acc"]) / dacc, 3)
+                out["thermal_limited_frac"] = round(
+                    (b["socket_thm_residency_acc"] - a["socket_thm_residency_acc"]) / dacc, 3)
+        except (TypeError, KeyError):
+            pass
+        return out
+
+
+def time_steps(step, stream, steps: int, warmup: int, settle_ms: float = 0.0, sampler=None):
+    """W untimed steps, then (untimed) more steps until `settle_ms` of wall
+    time has passed since the warm-up began, so that the clocks reach their
+    loaded steady state; then K steps between HIP events on the launch
+    stream.  Returns (per-step ms list, region ms, wall s, info) with info
+    holding the settle phase's length and, when a sampler runs, the clock
+    and power summary of the settle phase's last 500 ms and of the timed
+    region."""
     import torch
 
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    settle_steps = 0
+    while (time.perf_counter() - t_warm) * 1e3 < settle_ms:
+        for _ in range(8):
+            step()
+        settle_steps += 8
+        torch.cuda.synchronize()
+    t_settled = time.perf_counter()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -139,9 +274,38 @@ def time_steps(step, stream, steps: int, warmup: int):
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    wall = t1 - t0
     per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    return per, starts[0].elapsed_time(ends[-1]), wall
+    info = {"settle_ms": round((t_settled - t_warm) * 1e3, 1), "settle_steps": settle_steps,
+            "warmup_steps": warmup}
+    if sampler is not None:
+        time.sleep(3 * sampler.period)  # one more sample after the region ends
+        sampler.stop()
+        info["clocks_settle_last_500ms"] = sampler.window(t_settled - 0.5, t_settled)
+        # the sample just after the region closes it (the accumulators are
+        # differenced between the first and last samples of the window)
+        info["clocks_timed_region"] = sampler.window(t0, t1 + 3 * sampler.period)
+    return per, starts[0].elapsed_time(ends[-1]), wall, info
+
+
+def launch_spread(per):
+    """First and last five launch durations (ms) of the timed region."""
+    return {"first5_ms": [round(x, 4) for x in per[:5]],
+            "last5_ms": [round(x, 4) for x in per[-5:]]}
+
+
+def blas_info():
+    """The BLAS library numpy uses (name, version, threads) for the CPU
+    baseline record."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        return [{"library": p.get("internal_api"), "version": p.get("version"),
+                 "threads": p.get("num_threads"),
+                 "file": os.path.basename(p.get("filepath", ""))} for p in blas]
+    except Exception as e:  # pragma: no cover
+        return [{"error": str(e)}]
 
 
 def copy_calibration(mib: int, dev):
@@ -211,7 +375,9 @@ def run_decode(args) -> int:
             return 1
 
     stream = torch.cuda.current_stream(dev)
-    per, region_ms, wall = time_steps(step, stream, args.steps, args.warmup)
+    sampler = None if args.no_clock_sampler else GpuMetricsSampler().start()
+    per, region_ms, wall, tinfo = time_steps(step, stream, args.steps, args.warmup,
+                                             args.settle_ms, sampler)
     copy_calibration(args.copy_calibration_mib, dev)
     ms_per_step = region_ms / args.steps
     avg_ms = sum(per) / len(per)
@@ -243,7 +409,8 @@ def run_decode(args) -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "timing": {"avg_launch_ms": round(avg_ms, 4), "min_launch_ms": round(min(per), 4),
-                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3)},
+                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3),
+                   **launch_spread(per), **tinfo},
         "parity": parity,
     }
     if not args.no_cpu_baseline:
@@ -260,7 +427,7 @@ def run_decode(args) -> int:
             "value": cb / dt / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{done} of {B} sequences, all {H} query heads each; float64 numpy, "
                       f"scores and probabilities materialised; {dt:.1f} s wall",
-            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
+            "seconds": dt, "host_cpus": len(os.sched_getaffinity(0)), "blas": blas_info()}
     print(json.dumps(res), flush=True)
     return 0
 
@@ -333,11 +500,11 @@ def run_mat(args) -> int:
     stream = torch.cuda.current_stream(dev)
     steps = max(1, args.steps // 10)  # each step moves ~13 GB: a tenth of the steps
     warm = max(1, args.warmup // 10)
-    per, region_ms, wall = time_steps(step, stream, steps, warm)
+    per, region_ms, wall, tinfo = time_steps(step, stream, steps, warm)
     o2 = torch.empty_like(q)
     l2 = torch.empty_like(lse)
-    fper, _, _ = time_steps(lambda: ea.forward(q, k, v, causal=causal, scale=scale, out=o2,
-                                               lse=l2), stream, steps, warm)
+    fper, _, _, _ = time_steps(lambda: ea.forward(q, k, v, causal=causal, scale=scale, out=o2,
+                                                  lse=l2), stream, steps, warm)
     copy_calibration(args.copy_calibration_mib, dev)
     ms_per_step = region_ms / steps
     avg_ms = sum(per) / len(per)
@@ -369,7 +536,8 @@ def run_mat(args) -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(kname, name, "mat")},
         "timing": {"avg_launch_ms": round(avg_ms, 4), "min_launch_ms": round(min(per), 4),
-                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3)},
+                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3),
+                   **launch_spread(per), **tinfo},
         "compare": {"fused_fwd_avg_ms": round(fused_ms, 4),
                     "materialised_over_fused": round(avg_ms / fused_ms, 2)},
         "parity": parity,
@@ -397,6 +565,12 @@ def main() -> int:
                     help="heads (fwd, bwd) or sequences (decode) of the workload the CPU "
                          "oracle is timed on (default 32 for fwd, 2 for bwd and decode)")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=2000.0,
+                    help="untimed: keep stepping after the warm-up until this much wall "
+                         "time has passed since it began, so the clocks settle under load "
+                         "before the timed region (reported as timing.settle_ms)")
+    ap.add_argument("--no-clock-sampler", action="store_true",
+                    help="do not sample clocks and power (amdsmi) around the timed region")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -519,7 +693,9 @@ def main() -> int:
             return 1
 
     stream = torch.cuda.current_stream(dev)  # the launch stream of the binding
-    per_launch_ms, region_ms, wall = time_steps(step, stream, args.steps, args.warmup)
+    sampler = None if args.no_clock_sampler else GpuMetricsSampler().start()
+    per_launch_ms, region_ms, wall, tinfo = time_steps(step, stream, args.steps, args.warmup,
+                                                       args.settle_ms, sampler)
     ms_per_step = region_ms / args.steps
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
     copy_calibration(args.copy_calibration_mib, dev)
@@ -561,7 +737,7 @@ def main() -> int:
         "timing": {"avg_launch_ms": round(avg_launch_ms, 4),
                    "min_launch_ms": round(min(per_launch_ms), 4),
                    "max_launch_ms": round(max(per_launch_ms), 4),
-                   "wall_s": round(wall, 3)},
+                   "wall_s": round(wall, 3), **launch_spread(per_launch_ms), **tinfo},
         "parity": parity,
     }
     if not args.no_cpu_baseline:

@@ -22,7 +22,7 @@ __all__ = [
     "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_fwd_gqa",
     "attn_bwd_gqa", "attn_decode", "decode", "decode_workspace_bytes", "decode_splits",
     "attn_fwd_materialized", "forward_materialized",
-    "kernel_name", "fwd_kernel_name_for", "fwd_f32_kernel_name_for",
+    "kernel_name", "fwd_kernel_name_for", "fwd_f32_kernel_name_for", "decode_kernel_name_for",
     "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
     "LIB_PATH", "STATUS", "flops", "bwd_flops",
 ]
@@ -58,6 +58,7 @@ EXPORTS = {
     "attn_fwd_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
     "attn_fwd_f32_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
+    "attn_decode_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 6 + [ctypes.c_int]),
 }
 
 
@@ -111,6 +112,14 @@ def fwd_f32_kernel_name_for(B: int, H: int, T: int, d: int, causal: bool):
     """The fp32 forward instance attn_fwd_f32 launches for these sizes on
     the current device (needs a GPU)."""
     n = load_library().attn_fwd_f32_kernel_name_for(B, H, T, d, int(bool(causal)))
+    return None if n is None else n.decode()
+
+
+def decode_kernel_name_for(B: int, H: int, H_kv: int, Tq: int, Tk: int, d: int, causal: bool):
+    """The kernel attn_decode launches first for these sizes on the current
+    device: the split-key decode kernel or the forward instance that runs
+    over the cache (needs a GPU)."""
+    n = load_library().attn_decode_kernel_name_for(B, H, H_kv, Tq, Tk, d, int(bool(causal)))
     return None if n is None else n.decode()
 
 
@@ -175,6 +184,24 @@ def attn_fwd_materialized(q, k, v, o, lse, s_buf, p_buf, B, H, T, d, causal, sca
                                                 int(causal), float(scale), stream or None)
 
 
+def _check_buffer(t, name: str, shape, dtype, device) -> None:
+    """A caller-supplied output or scratch tensor must match exactly: the C
+    ABI receives only its address and cannot check its size."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be a {dtype} tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _check_same_device(ts, names: str) -> None:
+    dev = ts[0].device
+    if any(t.device != dev for t in ts):
+        raise ValueError(f"{names} must all be on the same device")
+
+
 def flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
     """Counted FLOPs of one forward: the two T x T x d contractions,
     4*T*T*d per head, halved under a causal mask."""
@@ -213,16 +240,15 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous CUDA tensors")
+    _check_same_device((q, k, v), "q, k, v")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    _check_buffer(out, "out", q.shape, q.dtype, q.device)
+    _check_buffer(lse, "lse", (B, H, T), torch.float32, q.device)
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     with torch.cuda.device(q.device):
         if q.dtype == torch.float32:
@@ -261,6 +287,7 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
     for t in ts + (lse,):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("all tensors must be contiguous CUDA tensors")
+    _check_same_device(ts + (lse,), "q, k, v, o, dout, lse")
     if lse.shape != (B, H, T) or lse.dtype != torch.float32:
         raise ValueError("lse must be a float32 [B, H, T] tensor")
     if scale is None:
@@ -270,11 +297,12 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
     dv = torch.empty_like(v) if dv is None else dv
     if ws is None:
         ws = torch.empty(2 * B * H * T, dtype=torch.float32, device=q.device)
-    for t, like in ((dq, q), (dk, k), (dv, v)):
-        if t.shape != like.shape or t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous bf16 tensors like q, k, v")
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check_buffer(t, name, like.shape, torch.bfloat16, q.device)
     if ws.numel() < 2 * B * H * T or ws.dtype != torch.float32 or not ws.is_contiguous():
         raise ValueError("ws must be a contiguous float32 tensor of 2*B*H*T elements")
+    if ws.device != q.device:
+        raise ValueError(f"ws must be on {q.device}")
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     with torch.cuda.device(q.device):
         st = attn_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
@@ -305,14 +333,19 @@ def decode(q, k_cache, v_cache, Tk: int | None = None, causal: bool = True,
     for t in (q, k_cache, v_cache):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q and the caches must be contiguous CUDA tensors")
+    _check_same_device((q, k_cache, v_cache), "q, k_cache, v_cache")
     Tk = Tcap if Tk is None else int(Tk)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_buffer(out, "out", q.shape, torch.bfloat16, q.device)
+    _check_buffer(lse, "lse", (B, H, Tq), torch.float32, q.device)
     need = decode_workspace_bytes(B, H, Hkv, Tq, Tk, d) if Hkv and Tk else 0
     if ws is None and need > 0:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if ws is not None and (not ws.is_contiguous() or ws.device != q.device):
+        raise ValueError(f"ws must be a contiguous tensor on {q.device}")
     ws_ptr = ws.data_ptr() if ws is not None else 0
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
@@ -339,6 +372,7 @@ def forward_materialized(q, k, v, causal: bool = True, scale: float | None = Non
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous CUDA tensors")
+    _check_same_device((q, k, v), "q, k, v")
     B, H, T, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -348,6 +382,10 @@ def forward_materialized(q, k, v, causal: bool = True, scale: float | None = Non
         s_buf = torch.empty((B, H, T, T), dtype=torch.float32, device=q.device)
     if p_buf is None:
         p_buf = torch.empty((B, H, T, T), dtype=torch.bfloat16, device=q.device)
+    _check_buffer(out, "out", q.shape, torch.bfloat16, q.device)
+    _check_buffer(lse, "lse", (B, H, T), torch.float32, q.device)
+    _check_buffer(s_buf, "s_buf", (B, H, T, T), torch.float32, q.device)
+    _check_buffer(p_buf, "p_buf", (B, H, T, T), torch.bfloat16, q.device)
     s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
     with torch.cuda.device(q.device):
         st = attn_fwd_materialized(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

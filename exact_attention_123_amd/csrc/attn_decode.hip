@@ -268,6 +268,20 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
   return ATTN_OK;
 }
 
+const char* attn_decode_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t Tq,
+                                        int64_t Tk, int64_t d, int causal) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || H % H_kv != 0) return nullptr;
+  if ((d != 64 && d != 128) || (causal != 0 && causal != 1)) return nullptr;
+  if (B > (int64_t(1) << 31) / H || Tq > (int64_t(1) << 30)) return nullptr;
+  if (check_device() != ATTN_OK) return nullptr;
+  if (over_forward(B, H, H_kv, Tq))
+    return attn_internal::fwd_over_cache_kernel_name(B, H, Tq, d, causal);
+  static const char* names[2][2] = {
+      {"attn_decode_bf16_d64_full_w4_blk32", "attn_decode_bf16_d64_causal_w4_blk32"},
+      {"attn_decode_bf16_d128_full_w4_blk32", "attn_decode_bf16_d128_causal_w4_blk32"}};
+  return names[d == 128 ? 1 : 0][causal];
+}
+
 int64_t attn_decode_splits(int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk) {
   if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || H % H_kv != 0) return 0;
   int64_t kps;

@@ -1193,6 +1193,14 @@ const void* f32_kernel(int64_t d, int causal) {
                 : (const void*)attn_fwd_f32_kernel<128, false>;
 }
 
+// Name of the 4-wave (128-row) bf16 instance.
+const char* w4_kernel_name(int64_t d, int causal) {
+  static const char* w4[2][2] = {
+      {"attn_fwd_bf16_d64_full_br128_bc64_w4", "attn_fwd_bf16_d64_causal_br128_bc64_w4"},
+      {"attn_fwd_bf16_d128_full_br128_bc64_w4", "attn_fwd_bf16_d128_causal_br128_bc64_w4"}};
+  return w4[d == 128 ? 1 : 0][causal ? 1 : 0];
+}
+
 }  // namespace
 
 namespace attn_internal {
@@ -1216,6 +1224,12 @@ attn_status fwd_over_cache(const void* q, const void* k, const void* v, void* o,
   const int nw = pick_plan(B, H, Tq, d) == FwdPlan::kWaves8 ? 8 : 4;
   return launch_bf16(nw, d, causal, scale, q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap,
                      causal ? Tk - Tq : 0, stream);
+}
+
+const char* fwd_over_cache_kernel_name(int64_t B, int64_t H, int64_t Tq, int64_t d, int causal) {
+  if (check_device() != ATTN_OK) return nullptr;
+  if (pick_plan(B, H, Tq, d) == FwdPlan::kWaves8) return attn_kernel_name(0, d, causal);
+  return w4_kernel_name(d, causal);
 }
 
 }  // namespace attn_internal
@@ -1280,9 +1294,6 @@ const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d,
   if (check_device() != ATTN_OK) return nullptr;
   const FwdPlan plan = pick_plan(B, H, T, d);
   if (plan == FwdPlan::kWaves8) return attn_kernel_name(0, d, causal);
-  static const char* w4[2][2] = {
-      {"attn_fwd_bf16_d64_full_br128_bc64_w4", "attn_fwd_bf16_d64_causal_br128_bc64_w4"},
-      {"attn_fwd_bf16_d128_full_br128_bc64_w4", "attn_fwd_bf16_d128_causal_br128_bc64_w4"}};
   static const char* rows[2][2][2] = {
       {{"attn_fwd_rows_bf16_d64_full_br32_bc32_w4", "attn_fwd_rows_bf16_d64_causal_br32_bc32_w4"},
        {"attn_fwd_rows_bf16_d128_full_br32_bc32_w4",
@@ -1291,7 +1302,7 @@ const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d,
        {"attn_fwd_rows_bf16_d128_full_br32_bc32_w8",
         "attn_fwd_rows_bf16_d128_causal_br32_bc32_w8"}}};
   if (plan == FwdPlan::kRows) return rows[rows_waves(T) == 8 ? 1 : 0][d == 128 ? 1 : 0][causal];
-  return w4[d == 128 ? 1 : 0][causal];
+  return w4_kernel_name(d, causal);
 }
 
 const char* attn_fwd_f32_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d,

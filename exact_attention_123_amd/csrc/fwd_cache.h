@@ -24,6 +24,10 @@ attn_status fwd_over_cache(const void* q, const void* k, const void* v, void* o,
                            int64_t Tk_cap, int64_t d, int causal, float scale,
                            hipStream_t stream);
 
+// Name of the forward instance fwd_over_cache launches for B H query heads
+// of Tq new rows (NULL when the current device is not a gfx950).
+const char* fwd_over_cache_kernel_name(int64_t B, int64_t H, int64_t Tq, int64_t d, int causal);
+
 }  // namespace attn_internal
 
 #endif  // ATTN_FWD_CACHE_H_

@@ -104,9 +104,13 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o,
                          hipStream_t stream);
 
 /*
- * float32 forward: the same contract with float elements in q, k, v, o.
- * Both contractions use fp32 MFMA (no reduced-precision inputs); P stays
- * fp32.
+ * float32 forward: the same operation ("Attention Mechanism: Computation &
+ * Memory Patterns", section 1; "Why Attention Is Difficult to Optimize",
+ * "The Attention Computation Flow") and the same contract as attn_fwd, with
+ * float elements in q, k, v, o.  Both contractions use fp32 MFMA (no
+ * reduced-precision inputs); P stays fp32, so one normaliser serves O and
+ * LSE.  A second exported symbol rather than a dtype argument, because the
+ * bf16 signature above is fixed; both are instances of one kernel design.
  */
 attn_status attn_fwd_f32(const float* q, const float* k, const float* v,
                          float* o, float* lse, int64_t B, int64_t H,
@@ -216,6 +220,21 @@ int64_t attn_decode_splits(int64_t B, int64_t H, int64_t H_kv, int64_t Tq,
                            int64_t Tk);
 
 /*
+ * Name of the kernel attn_decode launches first for these sizes on the
+ * current device: "attn_decode_bf16_d128_causal_w4_blk32" (and d64 / full
+ * variants) for the split-key kernel, or the forward instance (as
+ * attn_fwd_kernel_name_for names them) when the new queries are many enough
+ * for the forward kernel to run over the cache.  Lets a caller inspect the
+ * route actually taken for a decode or prefill chunk ("FlashAttention --
+ * avoid writing the giant intermediate", "Apply it at the right layer":
+ * check which backend was selected, and measure decode separately from
+ * prefill).  NULL if the sizes are invalid or the device is not a gfx950.
+ */
+const char* attn_decode_kernel_name_for(int64_t B, int64_t H, int64_t H_kv,
+                                        int64_t Tq, int64_t Tk, int64_t d,
+                                        int causal);
+
+/*
  * Materialised forward: the unfused three-kernel path that writes the T x T
  * score matrix S (fp32) and probability matrix P (bf16) to device memory and
  * reads them back ("Why Attention Is Difficult to Optimize", Figure 2: the
@@ -237,14 +256,23 @@ attn_status attn_fwd_materialized(const void* q, const void* k, const void* v,
                                   int64_t d, int causal, float scale,
                                   hipStream_t stream);
 
-/* Static description of a status code (never NULL). */
+/*
+ * Static description of a status code (never NULL).  Every unsupported
+ * request is reported by a code, never served by another path
+ * ("FlashAttention -- avoid writing the giant intermediate", "Apply it at
+ * the right layer": a requested option may be unsupported or fall back, so
+ * check what ran).
+ */
 const char* attn_status_string(attn_status s);
 
 /*
  * Name of the kernel instance attn_fwd (is_f32 = 0) or attn_fwd_f32
  * (is_f32 = 1) launches for head dimension d and the causal flag, e.g.
  * "attn_fwd_bf16_d128_causal_br256_bc64_w8", so that a caller can log which
- * kernel ran.  For bf16 this is the instance of grids with at least one
+ * kernel ran ("FlashAttention -- avoid writing the giant intermediate",
+ * "Apply it at the right layer": inspect the backend actually selected).
+ * The mask is part of the name because masked and unmasked problems run
+ * different instances.  For bf16 this is the instance of grids with at least one
  * 256-row workgroup per CU (smaller grids: see attn_fwd_kernel_name_for).  NULL if the combination
  * is unsupported.
  */

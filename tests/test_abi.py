@@ -252,3 +252,25 @@ def test_materialized_validation_errors():
     assert mat(s=0) == 1
     assert mat(p=A) == 6            # scratch overlaps q
     assert mat(T=0) == 0
+
+
+def test_binding_buffer_checks():
+    """The binding checks caller-supplied outputs and scratch buffers
+    (shape, dtype, contiguity, device) before it passes their addresses to
+    the C ABI, which cannot check sizes (CPU tensors stand in for device
+    ones here)."""
+    import torch
+    cpu = torch.device("cpu")
+    good = torch.empty((2, 3, 5, 64), dtype=torch.bfloat16)
+    ea._check_buffer(good, "out", (2, 3, 5, 64), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="shape"):
+        ea._check_buffer(good, "out", (2, 3, 6, 64), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="float32"):
+        ea._check_buffer(good, "lse", (2, 3, 5, 64), torch.float32, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        ea._check_buffer(good.transpose(2, 3).contiguous().transpose(2, 3), "out",
+                         (2, 3, 5, 64), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="must be on"):
+        ea._check_buffer(good.to("meta"), "s_buf", (2, 3, 5, 64), torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="same device"):
+        ea._check_same_device((good, good.to("meta")), "q, k")

@@ -183,3 +183,27 @@ def test_decode_full_size(name):
     B, H = w["B"], w["H"]
     heads = [(0, 0), (0, 3), (0, 4), (B - 1, H - 1), (B // 2, H // 2)]
     check(x, O, L, w["causal"], scale, w["Tk"], heads=heads)
+
+
+def test_decode_rejects_wrong_buffers():
+    """Caller-supplied out, lse and ws of the wrong shape, dtype or device
+    raise ValueError before any launch."""
+    import torch
+
+    import exact_attention_123_amd as ea
+    B, H, Hkv, Tq, Tk, d = 1, 8, 2, 1, 20000, 128
+    x = make_decode(B, H, Hkv, Tq, Tk, d, seed=8800)
+    q, k, v = (to_device(a, "bf16") for a in (x.q, x.k, x.v))
+    dev = q.device
+    with pytest.raises(ValueError, match="out"):
+        ea.decode(q, k, v, out=torch.empty((B, H, Tq + 1, d), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError, match="out"):
+        ea.decode(q, k, v, out=torch.empty((B, H, Tq, d), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError, match="lse"):
+        ea.decode(q, k, v, lse=torch.empty((B, H), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError, match="lse"):
+        ea.decode(q, k, v, lse=torch.empty((B, H, Tq), dtype=torch.float32))
+    with pytest.raises(ValueError, match="ws"):
+        ea.decode(q, k, v, ws=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ea.AttnError):  # too small: the library's own check
+        ea.decode(q, k, v, ws=torch.empty(16, dtype=torch.uint8, device=dev))

@@ -1,0 +1,193 @@
+"""GPU parity of the large-grid forward instances on their edge cases.
+
+The 8-wave (256 query rows per workgroup) and 4-wave (128 rows) bf16 forward
+kernels carry the headline workloads; each comes in two scale treatments
+(a positive scale folded into the exponent, any other scale multiplied into
+the scores before the mask).  Every case first asserts which instance the
+library launches for its sizes, then compares the output element by element
+with the float64 oracle at the bf16 tolerances (2e-2 on O, 1e-3 on LSE) on
+two full heads and on boundary rows (first and last rows of workgroups,
+the ragged end) of every head.
+
+Cases:
+  - scale in {0, -0.7/sqrt(d), 0.5/sqrt(d), 1/sqrt(d)}, causal and full, d in
+    {64, 128}, seeded N(0,1) inputs with Q and K times 2;
+  - score ramps and sawtooths (the rise, fall and saw patterns below): every
+    few key tiles the scores outgrow the running max, or the first keys
+    dominate and later weights underflow, which drives the rescaling of the
+    online softmax when a later block changes the maximum ("FlashAttention --
+    avoid writing the giant intermediate", "Tiling and an incremental
+    normalization");
+  - a ramp through attn_decode on the route that runs the forward kernel
+    over the cache (many new queries appended to a cache).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import to_device
+from seeded_inputs import bf16_bits_to_f32, f32_to_bf16_bits, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_LSE = 2e-2, 1e-3
+
+# (instance suffix, d) -> (B, H, T): grids that select that instance on a
+# 256-CU MI355X (T not a multiple of the row block: ragged end).
+GRIDS = {
+    ("w8", 64): (1, 32, 2000),
+    ("w8", 128): (1, 32, 2000),
+    ("w4", 64): (1, 12, 4000),
+    ("w4", 128): (1, 8, 4000),
+}
+SUFFIX = {"w8": "_br256_bc64_w8", "w4": "_br128_bc64_w4"}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def boundary_rows(T, block):
+    """First and last rows of every workgroup block, plus the ragged end."""
+    r = set()
+    for b0 in range(0, T, block):
+        r.update((b0, b0 + 1, b0 + 31, b0 + 32, min(b0 + block, T) - 1))
+    r.update((T - 2, T - 1))
+    return np.array(sorted(x for x in r if 0 <= x < T), dtype=np.int64)
+
+
+def check(qb, kb, vb, O, L, causal, scale, block, full_heads):
+    """Compare every head's boundary rows and the full rows of
+    `full_heads` with the oracle; returns the worst (O, LSE) errors."""
+    B, H, T, d = qb.shape
+    rows = boundary_rows(T, block)
+    eo = el = 0.0
+    for b in range(B):
+        for h in range(H):
+            r = None if h in full_heads else rows
+            ref = oracle.attention_head(f64(qb[b, h]), f64(kb[b, h]), f64(vb[b, h]),
+                                        causal=causal, scale=scale, rows=r)
+            got_o = O[b, h] if r is None else O[b, h, r]
+            got_l = L[b, h] if r is None else L[b, h, r]
+            assert np.isfinite(got_o).all() and np.isfinite(got_l).all(), (b, h)
+            eo = max(eo, float(np.abs(got_o - ref["O"]).max()))
+            el = max(el, float(np.abs(got_l - ref["LSE"]).max()))
+    return eo, el
+
+
+def run_forward(qb, kb, vb, causal, scale):
+    import torch
+
+    import exact_attention_123_amd as ea
+    q, k, v = (to_device(a, "bf16") for a in (qb, kb, vb))
+    o, lse = ea.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def expect_instance(inst, B, H, T, d, causal):
+    import exact_attention_123_amd as ea
+    name = ea.fwd_kernel_name_for(B, H, T, d, causal)
+    want = f"attn_fwd_bf16_d{d}_{'causal' if causal else 'full'}{SUFFIX[inst]}"
+    assert name == want, f"sizes {B}x{H}x{T} d={d} select {name}, expected {want}"
+    return name
+
+
+@pytest.mark.parametrize("scale_mult", [0.0, -0.7, 0.5, 1.0], ids=["s0", "sneg", "shalf", "s1"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("inst", ["w8", "w4"])
+def test_instance_scales(inst, d, causal, scale_mult):
+    B, H, T = GRIDS[(inst, d)]
+    name = expect_instance(inst, B, H, T, d, causal)
+    scale = scale_mult / math.sqrt(d)
+    say(f"[headline scales] {name} B={B} H={H} T={T} scale={scale:+.4f}")
+    x = make_qkv(B, H, T, d, dtype="bf16", seed=9100 + d + (7 if causal else 0), qk_mult=2.0)
+    O, L = run_forward(x.q, x.k, x.v, causal, scale)
+    block = 256 if inst == "w8" else 128
+    eo, el = check(x.q, x.k, x.v, O, L, causal, scale, block, full_heads={0, H - 1})
+    say(f"    max|O err|={eo:.3e} max|LSE err|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+def pattern(name, T):
+    """Key multipliers c_j: the score of key j is scale * 0.5 * d * c_j."""
+    j = np.arange(T, dtype=np.float64)
+    if name == "rise":
+        return j / T * 60.0
+    if name == "fall":
+        return (T - j) / T * 60.0
+    if name == "saw":
+        return np.where((j // 96) % 2 == 0, (j % 96) * 0.6, -(j % 96) * 0.6)
+    raise ValueError(name)
+
+
+def ramp_inputs(name, B, H, T, d, seed, Tq=None):
+    """Q rows all 0.5 (the last Tq positions when Tq is given), key j equal
+    to c_j in every component, V seeded N(0,1); bf16 bit patterns."""
+    c = pattern(name, T)
+    q = np.full((B, H, T if Tq is None else Tq, d), 0.5, dtype=np.float32)
+    k = np.broadcast_to(c[None, None, :, None], (B, H, T, d)).astype(np.float32)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    v = rng.standard_normal((B, H, T, d), dtype=np.float32)
+    return [f32_to_bf16_bits(np.ascontiguousarray(a)) for a in (q, k, v)]
+
+
+@pytest.mark.parametrize("name", ["rise", "fall", "saw"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("inst", ["w8", "w4"])
+def test_instance_running_max(inst, d, causal, name):
+    B, H, T = GRIDS[(inst, d)]
+    kname = expect_instance(inst, B, H, T, d, causal)
+    scale = 1.0 / math.sqrt(d)
+    say(f"[headline ramps] {kname} {name} B={B} H={H} T={T}")
+    qb, kb, vb = ramp_inputs(name, B, H, T, d, seed=9200 + d)
+    O, L = run_forward(qb, kb, vb, causal, scale)
+    ref0 = oracle.attention_head(f64(qb[0, 0]), f64(kb[0, 0]), f64(vb[0, 0]), causal=causal,
+                                 scale=scale, rows=np.array([T - 1]))
+    # the scores of one row span hundreds of log2 units
+    s = ref0["S"][np.isfinite(ref0["S"])]
+    assert np.ptp(s) * math.log2(math.e) > 100
+    block = 256 if inst == "w8" else 128
+    eo, el = check(qb, kb, vb, O, L, causal, scale, block, full_heads={0, H - 1})
+    say(f"    max|O err|={eo:.3e} max|LSE err|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("name", ["rise", "saw"])
+def test_decode_forward_route_running_max(name):
+    """Tq = 1024 new queries over a cache of 3000 keys, 64 heads: large
+    enough for attn_decode to run the 8-wave forward kernel over the cache
+    (key offset Tk - Tq)."""
+    import torch
+
+    import exact_attention_123_amd as ea
+    B, H, Tq, Tk, d = 1, 64, 1024, 3000, 128
+    kname = ea.decode_kernel_name_for(B, H, H, Tq, Tk, d, True)
+    assert kname == "attn_fwd_bf16_d128_causal_br256_bc64_w8", kname
+    assert ea.decode_workspace_bytes(B, H, H, Tq, Tk, d) == 0
+    say(f"[headline decode route] {kname} {name} H={H} Tq={Tq} Tk={Tk}")
+    scale = 1.0 / math.sqrt(d)
+    qb, kb, vb = ramp_inputs(name, B, H, Tk, d, seed=9300, Tq=Tq)
+    q, k, v = (to_device(a, "bf16") for a in (qb, kb, vb))
+    o, lse = ea.decode(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    O = o.float().cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    eo = el = 0.0
+    for h in range(H):  # every new row of every head (1024 x 3000 scores each)
+        ref = oracle.attention_decode_head(f64(qb[0, h]), f64(kb[0, h]), f64(vb[0, h]),
+                                           causal=True, scale=scale)
+        eo = max(eo, float(np.abs(O[0, h] - ref["O"]).max()))
+        el = max(el, float(np.abs(L[0, h] - ref["LSE"]).max()))
+    say(f"    max|O err|={eo:.3e} max|LSE err|={el:.3e}")
+    assert eo <= TOL_O and el <= TOL_LSE

@@ -74,3 +74,29 @@ def test_materialized_full_size():
         assert np.abs(L[0, h][rows] - ref["LSE"]).max() <= 1e-3
     assert np.abs(O - Of).max() <= 4e-2
     assert np.abs(L - Lf).max() <= 2e-3
+
+
+def test_materialized_rejects_wrong_buffers():
+    """Scratch S and P buffers and outputs of the wrong shape or dtype raise
+    ValueError before any launch."""
+    import torch
+
+    import exact_attention_123_amd as ea
+    B, H, T, d = 1, 2, 256, 64
+    x = make_qkv(B, H, T, d, dtype="bf16", seed=8900)
+    q, k, v = (to_device(a, "bf16") for a in (x.q, x.k, x.v))
+    dev = q.device
+    with pytest.raises(ValueError, match="s_buf"):
+        ea.forward_materialized(q, k, v, s_buf=torch.empty((B, H, T, T // 2),
+                                                            dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError, match="s_buf"):
+        ea.forward_materialized(q, k, v, s_buf=torch.empty((B, H, T, T), dtype=torch.bfloat16,
+                                                           device=dev))
+    with pytest.raises(ValueError, match="p_buf"):
+        ea.forward_materialized(q, k, v, p_buf=torch.empty((B, H, T, T), dtype=torch.float32,
+                                                           device=dev))
+    with pytest.raises(ValueError, match="out"):
+        ea.forward_materialized(q, k, v, out=torch.empty((B, H, T, d), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse"):
+        ea.forward_materialized(q, k, v, lse=torch.empty((B, H, T + 1), dtype=torch.float32,
+                                                         device=dev))
