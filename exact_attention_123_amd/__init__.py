@@ -83,6 +83,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise LibraryNotBuilt(
             f"{path} is missing; build it with `python -m exact_attention_123_amd.build`")
+    # One HIP runtime per process: torch ships its own libamdhip64 with the
+    # same soname as the system one the library links, and whichever loads
+    # first serves both.  Loading the library first would bind torch to the
+    # system runtime, and torch's device initialisation then fails; so torch
+    # loads first, and the library shares torch's runtime (and its streams).
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - torch is part of the environment
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in EXPORTS.items():
         fn = getattr(lib, name)

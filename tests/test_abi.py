@@ -274,3 +274,15 @@ def test_binding_buffer_checks():
         ea._check_buffer(good.to("meta"), "s_buf", (2, 3, 5, 64), torch.bfloat16, cpu)
     with pytest.raises(ValueError, match="same device"):
         ea._check_same_device((good, good.to("meta")), "q, k")
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library in a fresh process maps exactly one libamdhip64:
+    torch's (the binding imports torch before it loads the library)."""
+    code = ("import re, sys; sys.path.insert(0, %r); import exact_attention_123_amd as ea; "
+            "ea.load_library(); maps = open('/proc/self/maps').read(); "
+            "print(sorted(set(re.findall(r'/\\S*libamdhip64\\S*', maps))))" % ROOT)
+    out = subprocess.run([__import__("sys").executable, "-c", code], capture_output=True,
+                         text=True, check=True, timeout=300).stdout.strip()
+    libs = eval(out)
+    assert len(libs) == 1 and "/torch/lib/" in libs[0], libs
