@@ -140,7 +140,7 @@ class GpuMetricsSampler:
     fields None with the reason."""
 
     KEYS = ("current_gfxclks", "current_gfxclk", "current_uclk", "current_socket_power",
-            "energy_accumulator", "accumulation_counter", "ppt_residency_acc",
+            "accumulation_counter", "ppt_residency_acc",
             "socket_thm_residency_acc", "temperature_hotspot")
 
     def __init__(self, period_s: float = 0.004):
@@ -200,8 +200,8 @@ class GpuMetricsSampler:
     def window(self, t0: float, t1: float):
         """Summary of the samples taken in [t0, t1] (perf_counter seconds):
         median shader clock over the XCDs, memory clock, socket power, and
-        from the accumulators the average power and the fraction of the
-        window spent at the package power limit."""
+        from the residency accumulators the fraction of the window spent at
+        the package power limit (and at a thermal limit)."""
         if self.error and not self.samples:
             return {"error": self.error}
         sel = [(t, m) for t, m in self.samples if t0 <= t <= t1]
@@ -229,10 +229,6 @@ class GpuMetricsSampler:
                                      for _, m in sel), default=None)}
         (ta, a), (tb, b) = sel[0], sel[-1]
         try:
-            de = b["energy_accumulator"] - a["energy_accumulator"]
-            if tb > ta and de >= 0:
-                # the accumulator counts 15.259 uJ (2^-16 J) units
-                out["avg_power_w_from_energy"] = round(de * 15.259e-6 / (tb - ta), 1)
             dacc = b["accumulation_counter"] - a["accumulation_counter"]
             if dacc > 0:
                 out["ppt_limited_frac"] = round(

@@ -10,26 +10,24 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
-def sample(t, clks, power, energy, acc, ppt):
+def sample(t, clks, power, acc, ppt):
     return (t, {"current_gfxclks": clks, "current_gfxclk": 65535, "current_uclk": 1900,
-                "current_socket_power": power, "energy_accumulator": energy,
+                "current_socket_power": power,
                 "accumulation_counter": acc, "ppt_residency_acc": ppt,
                 "socket_thm_residency_acc": 0, "temperature_hotspot": 80})
 
 
 def test_sampler_window_summary():
     s = bench.GpuMetricsSampler()
-    # 8 XCD clocks, one unused slot (65535) ignored; 1 J per 0.1 s = 10 W
-    joule = int(round(1 / 15.259e-6))
-    s.samples = [sample(0.0, [2000] * 8 + [65535], 1000, 0, 0, 0),
-                 sample(0.05, [1800] * 8 + [65535], 1100, joule // 2, 50, 25),
-                 sample(0.10, [1900] * 8 + [65535], 1200, joule, 100, 100),
-                 sample(0.50, [100] * 8, 100, 10 * joule, 500, 100)]
+    # 8 XCD clocks, one unused slot (65535) ignored
+    s.samples = [sample(0.0, [2000] * 8 + [65535], 1000, 0, 0),
+                 sample(0.05, [1800] * 8 + [65535], 1100, 50, 25),
+                 sample(0.10, [1900] * 8 + [65535], 1200, 100, 100),
+                 sample(0.50, [100] * 8, 100, 500, 100)]
     w = s.window(0.0, 0.11)
     assert w["samples"] == 3
     assert w["sclk_mhz_median"] == 1900 and w["sclk_mhz_min"] == 1800
     assert w["mclk_mhz_median"] == 1900 and w["socket_power_w_median"] == 1100
-    assert abs(w["avg_power_w_from_energy"] - 10.0) < 0.1
     assert w["ppt_limited_frac"] == 1.0 and w["thermal_limited_frac"] == 0.0
     assert s.window(1.0, 2.0) == {"samples": 0}
 
