@@ -20,7 +20,8 @@ import os
 
 __all__ = [
     "forward", "backward", "attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_fwd_gqa",
-    "attn_bwd_gqa", "attn_decode", "decode", "decode_workspace_bytes", "decode_splits",
+    "attn_bwd_gqa", "attn_decode", "attn_decode_noalloc", "DECODE_NOALLOC_MAX_BYTES", "decode",
+    "decode_workspace_bytes", "decode_splits",
     "attn_fwd_materialized", "forward_materialized",
     "kernel_name", "fwd_kernel_name_for", "fwd_f32_kernel_name_for", "decode_kernel_name_for",
     "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
@@ -49,6 +50,8 @@ EXPORTS = {
                      + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_decode": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int64] * 8
                     + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
+    "attn_decode_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 7
+                            + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
     "attn_decode_workspace_bytes": (ctypes.c_int64, [ctypes.c_int64] * 6),
     "attn_decode_splits": (ctypes.c_int64, [ctypes.c_int64] * 5),
     "attn_fwd_materialized": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 4
@@ -176,6 +179,19 @@ def attn_decode(q, k, v, o, lse, ws, ws_bytes, B, H, H_kv, Tq, Tk, Tk_cap, d, ca
     """Raw decode entry point: integer device addresses, returns the status."""
     return load_library().attn_decode(q, k, v, o, lse, ws or None, ws_bytes, B, H, H_kv, Tq, Tk,
                                       Tk_cap, d, int(causal), float(scale), stream or None)
+
+
+def attn_decode_noalloc(q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap, d, causal, scale,
+                        stream=0) -> int:
+    """Raw decode entry point that allocates nothing (the library's own
+    device scratch of DECODE_NOALLOC_MAX_BYTES holds the split results):
+    integer device addresses, returns the status."""
+    return load_library().attn_decode_noalloc(q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap, d,
+                                              int(causal), float(scale), stream or None)
+
+
+# Size of the device scratch of attn_decode_noalloc (ATTN_DECODE_NOALLOC_MAX_BYTES).
+DECODE_NOALLOC_MAX_BYTES = 8 << 20
 
 
 def decode_workspace_bytes(B: int, H: int, H_kv: int, Tq: int, Tk: int, d: int) -> int:

@@ -39,6 +39,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "fwd_cache.h"
@@ -202,27 +203,12 @@ const void* decode_kernel(int causal) {
                 : (const void*)attn_decode_kernel<D, false>;
 }
 
-}  // namespace
-
-extern "C" {
-
-int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
-                                    int64_t d) {
-  if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || (d != 64 && d != 128)) return 0;
-  if (H % H_kv != 0) return 0;
-  int64_t kps;
-  const int64_t n = splits_for(B, H, H_kv, Tq, Tk, &kps);
-  return n > 1 ? n * B * H * Tq * (d + 1) * 4 : 0;
-}
-
-attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                        void* ws, int64_t ws_bytes, int64_t B, int64_t H, int64_t H_kv,
-                        int64_t Tq, int64_t Tk, int64_t Tk_cap, int64_t d, int causal,
-                        float scale, hipStream_t stream) {
-  bool empty;
-  attn_status st = validate(q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap, d, causal, scale,
-                            empty);
-  if (st != ATTN_OK || empty) return st;
+// Both decode entry points after validation: ws (ws_bytes) holds the split
+// partial results when there is more than one split.
+attn_status decode_launch(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* ws, int64_t ws_bytes, int64_t B, int64_t H, int64_t H_kv,
+                          int64_t Tq, int64_t Tk, int64_t Tk_cap, int64_t d, int causal,
+                          float scale, hipStream_t stream) {
   int64_t kps;
   const int64_t nchunk = row_chunks(Tq, H / H_kv);
   const int64_t nsplit = splits_for(B, H, H_kv, Tq, Tk, &kps);
@@ -240,6 +226,7 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
     part_o = (float*)ws;
     part_lse = part_o + nsplit * NR * d;
   }
+  attn_status st;
   if ((st = check_device()) != ATTN_OK) return st;
   if (over_forward(B, H, H_kv, Tq))
     return attn_internal::fwd_over_cache(q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap, d, causal,
@@ -266,6 +253,77 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o, fl
       return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
+}
+
+// Device scratch of attn_decode_noalloc (the split partial results), for
+// callers that cannot allocate.  Each device the library runs on holds its
+// own copy from the time the library's code object is loaded on it until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is ever passed to
+// a kernel.
+constexpr int64_t kScratchBytes = ATTN_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on the first
+// call on each device).
+attn_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return ATTN_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                                    int64_t d) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || Tq <= 0 || Tk <= 0 || (d != 64 && d != 128)) return 0;
+  if (H % H_kv != 0) return 0;
+  int64_t kps;
+  const int64_t n = splits_for(B, H, H_kv, Tq, Tk, &kps);
+  return n > 1 ? n * B * H * Tq * (d + 1) * 4 : 0;
+}
+
+attn_status attn_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                        void* ws, int64_t ws_bytes, int64_t B, int64_t H, int64_t H_kv,
+                        int64_t Tq, int64_t Tk, int64_t Tk_cap, int64_t d, int causal,
+                        float scale, hipStream_t stream) {
+  bool empty;
+  attn_status st = validate(q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap, d, causal, scale,
+                            empty);
+  if (st != ATTN_OK || empty) return st;
+  return decode_launch(q, k, v, o, lse, ws, ws_bytes, B, H, H_kv, Tq, Tk, Tk_cap, d, causal,
+                       scale, stream);
+}
+
+attn_status attn_decode_noalloc(const void* q, const void* k, const void* v, void* o,
+                                float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t Tq,
+                                int64_t Tk, int64_t Tk_cap, int64_t d, int causal, float scale,
+                                hipStream_t stream) {
+  bool empty;
+  attn_status st = validate(q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap, d, causal, scale,
+                            empty);
+  if (st != ATTN_OK || empty) return st;
+  if (attn_decode_workspace_bytes(B, H, H_kv, Tq, Tk, d) > kScratchBytes)
+    return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != ATTN_OK) return st;
+  return decode_launch(q, k, v, o, lse, ws, kScratchBytes, B, H, H_kv, Tq, Tk, Tk_cap, d, causal,
+                       scale, stream);
 }
 
 const char* attn_decode_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t Tq,

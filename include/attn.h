@@ -209,6 +209,33 @@ attn_status attn_decode(const void* q, const void* k, const void* v, void* o,
                         int64_t Tk_cap, int64_t d, int causal, float scale,
                         hipStream_t stream);
 
+/*
+ * Decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid allocation).  Same computation,
+ * kernels, arguments and errors as attn_decode, except that the split
+ * partial results go to a scratch buffer of ATTN_DECODE_NOALLOC_MAX_BYTES
+ * bytes that the library holds in device memory, one per GPU it runs on,
+ * until the process ends.  Problems whose attn_decode_workspace_bytes(...)
+ * exceeds that size are rejected with ATTN_ERR_WORKSPACE before anything is
+ * enqueued: splits x B x H x Tq may be at most 8 MiB / (4 (d + 1)), 16,256
+ * at d = 128 (16 sequences x 32 query heads x 1 query over 32768 keys take
+ * 4 splits and 264 KiB; a grid of at least 256 workgroups without splits
+ * needs none).  The buffer is fully rewritten by each call before
+ * it is read, so nothing needs clearing; but every call on one GPU shares
+ * it: calls that can overlap on one GPU (different streams, or host threads
+ * without ordering) race and must be serialised by the caller.  The first
+ * call on each device looks up the buffer's address (no allocation) with
+ * that device current.
+ */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES (8 << 20)
+
+attn_status attn_decode_noalloc(const void* q, const void* k, const void* v,
+                                void* o, float* lse, int64_t B, int64_t H,
+                                int64_t H_kv, int64_t Tq, int64_t Tk,
+                                int64_t Tk_cap, int64_t d, int causal,
+                                float scale, hipStream_t stream);
+
 /* Workspace bytes attn_decode needs for these sizes (0 if none, or if the
  * sizes are invalid). */
 int64_t attn_decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv,

@@ -286,3 +286,30 @@ def test_library_shares_torchs_hip_runtime():
                          text=True, check=True, timeout=300).stdout.strip()
     libs = eval(out)
     assert len(libs) == 1 and "/torch/lib/" in libs[0], libs
+
+
+@no_gpu_only
+def test_decode_noalloc_validation_errors():
+    """The allocation-free decode validates like attn_decode and rejects a
+    problem whose split results exceed its device scratch before any HIP
+    call."""
+    def dec(**kw):
+        a = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=8, Hkv=2, Tq=1, Tk=100,
+                 Tcap=100, d=128, causal=1, scale=0.1)
+        a.update(kw)
+        return ea.attn_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                      a["H"], a["Hkv"], a["Tq"], a["Tk"], a["Tcap"], a["d"],
+                                      a["causal"], a["scale"])
+    assert dec(Hkv=3) == 2
+    assert dec(d=96) == 3
+    assert dec(q=0) == 1
+    assert dec(causal=2) == 6
+    assert dec(Tq=0) == 0
+    # 300 heads x 32 queries, 2 splits: 2 * 9600 rows * 129 * 4 B = 9.9 MB > 8 MiB
+    big = dict(B=1, H=300, Hkv=300, Tq=32, Tk=8192, Tcap=8192, q=1 << 36, k=2 << 36,
+               v=3 << 36, o=4 << 36, lse=5 << 36)
+    assert ea.decode_workspace_bytes(1, 300, 300, 32, 8192, 128) > ea.DECODE_NOALLOC_MAX_BYTES
+    assert dec(**big) == 9
+    header = open(HEADER).read()
+    assert re.search(r"#define ATTN_DECODE_NOALLOC_MAX_BYTES \(8 << 20\)", header)
+    assert ea.DECODE_NOALLOC_MAX_BYTES == 8 << 20
