@@ -52,12 +52,7 @@
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+using namespace attn_tiles;
 
 // fp32 kernel: 4 waves, 128 query rows per workgroup (32 per wave).
 constexpr int kThreads = 256;
@@ -66,34 +61,11 @@ constexpr int kBR = 128;
 // waves and 128 rows when the 8-wave grid has fewer workgroups than the GPU
 // has CUs (see pick_plan, which sends the smallest problems to the
 // row-chunk kernel instead).
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
-
-// Raw buffer descriptor over `bytes` bytes at `base`.  Loads through it whose
-// byte range lies past `bytes` return zero instead of touching memory, which
-// is how the ragged end of the sequence (keys or queries >= T) is read as
-// zero without branches.  Word 3 (0x00020000) is the raw-buffer format word
-// of the gfx9 family.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
-}
-
-// Row of the 32-row MFMA operand tile that lane row i feeds with key
-// (swap bits 2 and 3 of i).  With this order the accumulator registers
-// r = 8a..8a+7 of lane half h hold keys 16a + 8h + 0..7, i.e. eight
-// consecutive keys, which is what one B-operand slot of the PV MFMA wants.
-__device__ __forceinline__ int key_row_perm(int i) {
-  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
-}
 
 // Key offset (within a 32-key block) held by accumulator register r of lane
-// half h, for the bf16 kernel (permuted rows) and the fp32 kernel (plain).
+// half h, for the bf16 kernel (K rows fed in attn_tiles::row_perm order, so
+// that registers 8a..8a+7 of lane half h hold eight consecutive keys, one
+// B-operand slot of the PV MFMA) and the fp32 kernel (plain order).
 __host__ __device__ constexpr int acc_key_perm(int r, int h) {
   return 16 * (r / 8) + 8 * h + 4 * ((r / 4) & 1) + (r & 3);
 }
@@ -121,25 +93,8 @@ __device__ __forceinline__ void block_coords(int BH, int nqb, int G, int& bhq, i
   bhq = bhkv * G + hid / nkv;
 }
 
-// Max of x over the lane pair (l, l ^ 32) that holds one query's scores.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Rescaling threshold of the running max, in log2 units.  The running max m
-// is only raised when a tile's max exceeds it by more than this, so p =
-// exp2(c*s - m) stays below 2^kLazyRescale and the output accumulator and
-// normaliser are rescaled only on those (rare, wave-uniform) occasions.  The
-// result is the same softmax: the common factor cancels in acc / l.  With
-// 2^64 as the largest weight, the normaliser stays below 2^64 * T < 2^96 and
-// the accumulator below 2^96 * max|v|, far inside fp32 (and bf16) range, and
-// relative rounding is the same as with an exact max.  Weights more than
-// 2^126 below the stale max flush to zero; relative to the true max they are
-// smaller still, so they are negligible either way.
-constexpr float kLazyRescale = 64.0f;
-// Bound on a lane's sum of one sub-tile's weights in the bf16 kernel (see
+// Lazy running max of the large-grid bf16 kernel.  Bound on a lane's sum of
+// one sub-tile's weights (see
 // its softmax): above it the running max is raised.  kRegrow: once some lane
 // passed the bound, every row whose sub-tile max exceeds its running max by
 // more than this gets the sub-tile max as its new running max (a row that
@@ -197,9 +152,6 @@ __device__ __forceinline__ void online_softmax_update(f32x16_t (&s)[NKT], float 
 // ---------------------------------------------------------------------------
 // bf16 kernel
 // ---------------------------------------------------------------------------
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 template <int D, int NW_ = 8>
 struct Bf16Tile {
@@ -411,7 +363,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   // swizzle has period 16 in the row, so the half adds a plain offset).
   int kaddr[NDS];
   {
-    const int r = key_row_perm(j);
+    const int r = row_perm(j);
     const int f = attn_tiles::swz<D>(r);
 #pragma unroll
     for (int s = 0; s < NDS; ++s) kaddr[s] = r * RB + 16 * ((2 * s + h) ^ f);
@@ -437,11 +389,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   f32x16_t oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x16_t{};
-  // The running max starts at a finite value far below any score in log2
-  // units (|scores| <= 2^127 * |c|): the first visible sub-tile always
-  // raises it (alpha = exp2(-huge) = 0), and masked scores (-inf) still give
-  // weight exp2(-inf) = 0.
-  constexpr float kMinusHuge = -1e38f;
+  // The running max starts at kMinusHuge (see attn_tiles): the first visible
+  // sub-tile always raises it, and masked scores (-inf) give weight 0.
   float m_run = kMinusHuge, l_run = 0.0f, w_run = 0.0f;
   const float cm = PRESCALE ? 1.0f : c;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};

@@ -40,17 +40,8 @@ constexpr int kWaves = 4;  // waves per workgroup unless the caller picks NW
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlk = 32;      // keys per block (one MFMA score tile)
 constexpr int kMaxRows = 32;  // query rows of one workgroup (one MFMA column block)
-// Running-max threshold (log2 units), as in the forward: the max is raised
-// only when a block's max exceeds it by more than this, so weights stay
-// below 2^64 and sums of at most 2^17 of them far inside fp32.
-constexpr float kLazyRescale = 64.0f;
-constexpr float kMinusHuge = -1e38f;
-
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
-                                                  false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// The running max follows the max-threshold rule of attn_tiles
+// (kLazyRescale).
 
 // Body of a kernel of 64 NW threads (NW waves share the keys of the
 // chunk).  Workgroup (row chunk, kv head

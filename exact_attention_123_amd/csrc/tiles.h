@@ -1,7 +1,9 @@
-// Device helpers shared by the backward and decode kernels: raw buffer
-// descriptors, and a swizzled LDS layout for tiles of D-wide bf16 rows that
-// are read both row-wise (A operand of a score MFMA) and column-wise with the
-// transposing LDS read (A operand of a contraction over the rows).
+// Device helpers shared by every kernel of the library: vector types,
+// constants, hardware exp2/log2, raw buffer descriptors, the lane-pair max
+// and lazy-max constants of the online softmax, and a swizzled LDS layout
+// for tiles of D-wide bf16 rows that are read both row-wise (A operand of a
+// score MFMA) and column-wise with the transposing LDS read (A operand of a
+// contraction over the rows).
 #ifndef ATTN_TILES_H_
 #define ATTN_TILES_H_
 
@@ -27,6 +29,27 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Max of x over the lane pair (l, l ^ 32) that holds one query's scores in
+// the transposed score tile of a 32x32 MFMA.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Lazy running max of the online softmax, max-threshold form (the row-chunk
+// and fp32 kernels; the large-grid bf16 forward bounds each lane's weight
+// sum instead): the running max m (log2 units) is raised only when a
+// block's max exceeds it by more than kLazyRescale, so every weight
+// exp2(s - m) stays below 2^64, a normaliser of at most 2^17 such weights
+// far inside fp32, and the accumulators are rescaled only on those rare,
+// wave-uniform occasions.  The common factor cancels in acc / l.
+constexpr float kLazyRescale = 64.0f;
+// Initial running max: finite and far below any score in log2 units, so
+// the first visible block always raises it (exp2(-huge - x) = 0 rescales an
+// empty accumulator) while masked scores (-inf) still give weight 0.
+constexpr float kMinusHuge = -1e38f;
 
 // Raw buffer descriptor over `bytes` bytes at `base`: loads past the end
 // return zero without touching memory (ragged ends of the sequence).
