@@ -2,11 +2,13 @@
 
     python -m exact_attention_123_amd.build
 
-compiles ``csrc/attn_fwd.hip`` (forward), ``csrc/attn_bwd.hip`` (backward) and
+compiles ``csrc/attn_fwd.hip`` (forward), ``csrc/attn_bwd.hip`` (backward),
 ``csrc/attn_decode.hip`` (decode over a key/value cache) and
 ``csrc/attn_materialized.hip`` (the unfused three-kernel forward) with hipcc into
-``exact_attention_123_amd/libattn.so``.  The library exports the C ABI of
-``include/attn.h``; the Python binding loads it with ctypes.
+``exact_attention_123_amd/libattn.so``, and the same sources with
+``-DATTN_DEBUG_BARRIERS`` into ``libattn_debug_barriers.so`` (race check).
+The library exports the C ABI of ``include/attn.h``; the Python binding loads
+it with ctypes.
 """
 from __future__ import annotations
 
@@ -21,6 +23,9 @@ SRCS = [os.path.join(PKG, "csrc", n)
         for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_materialized.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
+# The same library built with -DATTN_DEBUG_BARRIERS (extra workgroup barriers
+# at every key/value tile, for the bitwise race check of the GPU tests).
+DEBUG_LIB = os.path.join(PKG, "libattn_debug_barriers.so")
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [
@@ -45,10 +50,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
-def build(verbose: bool = False, out: str = LIB) -> str:
-    """Compile the library; returns its path.  Raises on compiler errors."""
+def build(verbose: bool = False, out: str = LIB, debug_barriers: bool = False) -> str:
+    """Compile the library (with debug_barriers: the race-check build);
+    returns its path.  Raises on compiler errors."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
+    extra = ["-DATTN_DEBUG_BARRIERS"] if debug_barriers else []
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,3 +73,4 @@ def build(verbose: bool = False, out: str = LIB) -> str:
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, out=DEBUG_LIB, debug_barriers=True))

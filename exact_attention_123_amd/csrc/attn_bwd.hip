@@ -248,11 +248,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
   // one tile.
   for (int it = 0; it < nit; it += 2) {
     if (it + 1 < nit) stage(sQ1, sG1, sL1, sD1, (it + 1) / per, qt0 + (it + 1) % per);
+    ATTN_DEBUG_SYNC();
     tile(sQ0, sG0, sL0, sD0, it);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     if (it + 1 >= nit) break;
     if (it + 2 < nit) stage(sQ0, sG0, sL0, sD0, (it + 2) / per, qt0 + (it + 2) % per);
+    ATTN_DEBUG_SYNC();
     tile(sQ1, sG1, sL1, sD1, it + 1);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
@@ -376,11 +378,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   // Two tiles per trip, alternating the stages (see the dK/dV kernel).
   for (int t = 0; t < nkt; t += 2) {
     if (t + 1 < nkt) stage(sK1, sV1, t + 1);
+    ATTN_DEBUG_SYNC();
     tile(sK0, sV0, t);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 >= nkt) break;
     if (t + 2 < nkt) stage(sK0, sV0, t + 2);
+    ATTN_DEBUG_SYNC();
     tile(sK1, sV1, t + 1);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);

@@ -581,10 +581,12 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
     char* vfree = R == 0 ? sV2 : R == 1 ? sV0 : sV1;
     dma_k(kfree, tau + 3);
     dma_v(vfree, tau + 2);
+    ATTN_DEBUG_SYNC();
     if (tau < tskip) {
       substep(std::true_type{}, kcur, 0, vcur, 0, sY, sX, pX, pY, 2 * tau + 1);
       substep(std::true_type{}, kcur, 1, vcur, 1, sX, sY, pY, pX, 2 * tau + 2);
     }
+    ATTN_DEBUG_SYNC();
     // Every wave issued KPER + VPER loads this iteration: waiting down to
     // that many in flight means K_{tau+2} and V_{tau+1} have landed.
     wait_dma(std::integral_constant<int, KPER + VPER>{});

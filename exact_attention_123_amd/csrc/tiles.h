@@ -12,6 +12,20 @@
 #include <cstdint>
 #include <cstring>
 
+// Race check.  Built with -DATTN_DEBUG_BARRIERS, the kernels add full
+// workgroup barriers (every wave's loads, stores and LDS operations
+// complete, then all waves meet) at points that every wave of a workgroup
+// reaches: after each key/value tile's loads are issued and after its
+// compute.  A correct kernel gives bitwise the same results either way
+// (same arithmetic, same order); a missing wait shows as a difference.
+#ifdef ATTN_DEBUG_BARRIERS
+#define ATTN_DEBUG_SYNC() __syncthreads()
+#else
+#define ATTN_DEBUG_SYNC() \
+  do {                     \
+  } while (0)
+#endif
+
 namespace attn_tiles {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

@@ -313,3 +313,14 @@ def test_decode_noalloc_validation_errors():
     header = open(HEADER).read()
     assert re.search(r"#define ATTN_DECODE_NOALLOC_MAX_BYTES \(8 << 20\)", header)
     assert ea.DECODE_NOALLOC_MAX_BYTES == 8 << 20
+
+
+def test_debug_barriers_build_exports_the_same_symbols():
+    """The race-check build (-DATTN_DEBUG_BARRIERS) exists next to the
+    library and exports every declared function."""
+    path = os.path.join(os.path.dirname(ea.LIB_PATH), "libattn_debug_barriers.so")
+    assert os.path.exists(path), "build() compiles the race-check library too"
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(declared_functions()) <= exported
