@@ -35,6 +35,11 @@ shader and memory clocks, socket power and power-limit residency sampled
 (amdsmi, host-side) over the settle phase's last 500 ms and over the timed
 region.
 
+After the timed region the library's MFMA-only probe measures the bf16
+matrix-core rate this GPU sustains with nothing else running
+(``mfma_ceiling``: TFLOP/s, its clock, and the pass's fraction of it), a
+secondary denominator next to the published dense peak.
+
 Prints one JSON line with the throughput, the roofline position of the pass
 (MFMA-bound, against MI355X's dense bf16 peak; for the backward the three
 kernels of one call are timed together) and the float64 CPU oracle timed on a
@@ -283,6 +288,43 @@ def time_steps(step, stream, steps: int, warmup: int, settle_ms: float = 0.0, sa
         # differenced between the first and last samples of the window)
         info["clocks_timed_region"] = sampler.window(t0, t1 + 3 * sampler.period)
     return per, starts[0].elapsed_time(ends[-1]), wall, info
+
+
+def mfma_ceiling(dev, sampler=None, shape: int = 0):
+    """The measured matrix-core ceiling: the library's MFMA-only probe
+    (independent bf16 accumulation chains on register operands, 4 waves per
+    workgroup, 8 workgroups per CU), timed with HIP events on its stream
+    after one untimed launch.  Returns TFLOP/s and, with a sampler, the
+    shader clock during the probe."""
+    import torch
+
+    import exact_attention_123_amd as ea
+
+    lib = ea.load_library()
+    wg = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+    iters = 8000
+    sink = torch.empty(wg * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    if lib.attn_probe_mfma(shape, wg, iters, sink.data_ptr(), s) != 0:
+        return {"error": "probe launch failed"}
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(3):
+        lib.attn_probe_mfma(shape, wg, iters, sink.data_ptr(), s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = e0.elapsed_time(e1) / 3
+    out = {"tflops": round(lib.attn_probe_mfma_flops(shape, wg, iters) / (ms * 1e-3) / 1e12, 1),
+           "instruction": ("v_mfma_f32_32x32x16_bf16" if shape == 0
+                           else "v_mfma_f32_16x16x32_bf16"),
+           "avg_launch_ms": round(ms, 3)}
+    if sampler is not None:
+        out["clocks"] = sampler.window(t0, t1)
+    return out
 
 
 def launch_spread(per):
@@ -567,6 +609,9 @@ def main() -> int:
                          "before the timed region (reported as timing.settle_ms)")
     ap.add_argument("--no-clock-sampler", action="store_true",
                     help="do not sample clocks and power (amdsmi) around the timed region")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the MFMA-only probe (the measured ceiling reported next to "
+                         "the published peak)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (for counter calibration)")
     args = ap.parse_args()
@@ -696,9 +741,20 @@ def main() -> int:
     avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
     copy_calibration(args.copy_calibration_mib, dev)
 
+    ceiling = None
+    if dt == "bf16" and not args.no_mfma_ceiling:
+        psampler = None if args.no_clock_sampler else GpuMetricsSampler().start()
+        ceiling = mfma_ceiling(dev, psampler)
+        if psampler is not None:
+            time.sleep(3 * psampler.period)
+            psampler.stop()
+            ceiling["clocks"] = psampler.window(0.0, time.perf_counter())
+
     value = fl / (ms_per_step * 1e-3) / 1e12
     achieved = fl / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dt]
+    if ceiling is not None and ceiling.get("tflops"):
+        ceiling["frac"] = round(achieved / ceiling["tflops"], 4)
     traffic = measured_traffic(kname, args.workload, args.pass_)
 
     config = {"workload": args.workload + (("_causal" if causal else "_full")
@@ -736,6 +792,10 @@ def main() -> int:
                    "wall_s": round(wall, 3), **launch_spread(per_launch_ms), **tinfo},
         "parity": parity,
     }
+    if ceiling is not None:
+        # secondary denominator: the bf16 MFMA rate this GPU sustains with
+        # nothing else running (untimed, after the timed region)
+        res["mfma_ceiling"] = ceiling
     if not args.no_cpu_baseline:
         heads = args.cpu_heads if args.cpu_heads is not None else (2 if bwd else 32)
         res["cpu_baseline"] = cpu_baseline(x, causal, scale, min(heads, B * H), args.pass_,

@@ -36,7 +36,7 @@ STATUS = {
     8: "ATTN_ERR_LAUNCH", 9: "ATTN_ERR_WORKSPACE",
 }
 
-# The C prototypes from include/attn.h.
+# The C prototypes from include/attn.h and include/attn_probe.h.
 EXPORTS = {
     "attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4
                  + [ctypes.c_int, ctypes.c_float, ctypes.c_void_p]),
@@ -62,6 +62,10 @@ EXPORTS = {
     "attn_fwd_f32_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
     "attn_decode_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 6 + [ctypes.c_int]),
+    # include/attn_probe.h
+    "attn_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_void_p]),
+    "attn_probe_mfma_flops": (ctypes.c_double, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]),
 }
 
 

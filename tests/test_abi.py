@@ -37,9 +37,14 @@ no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer checks run
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    """Every function the headers under include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(os.path.dirname(HEADER))):
+        if h.endswith(".h"):
+            text = open(os.path.join(os.path.dirname(HEADER), h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_exports():
@@ -324,3 +329,17 @@ def test_debug_barriers_build_exports_the_same_symbols():
                          check=True).stdout
     exported = set(re.findall(r"\bT (attn_\w+)", out))
     assert set(declared_functions()) <= exported
+
+
+@no_gpu_only
+def test_probe_validation_and_flop_count():
+    assert ea.load_library().attn_probe_mfma(2, 1, 1, A, None) == 6
+    assert ea.load_library().attn_probe_mfma(0, 0, 1, A, None) == 2
+    assert ea.load_library().attn_probe_mfma(0, 1, 0, A, None) == 2
+    assert ea.load_library().attn_probe_mfma(0, 1, 1, None, None) == 1
+    assert ea.load_library().attn_probe_mfma(0, 1, 1, A + 2, None) == 5
+    f = ea.load_library().attn_probe_mfma_flops
+    # 4 waves x iters x (16 MFMAs of 32x32x16 | 32 of 16x16x32) x 2 m n k
+    assert f(0, 3, 10) == 3 * 4 * 10 * 16 * 2 * 32 * 32 * 16
+    assert f(1, 3, 10) == 3 * 4 * 10 * 32 * 2 * 16 * 16 * 32
+    assert f(5, 3, 10) == 0.0
