@@ -73,21 +73,40 @@ __host__ __device__ constexpr int acc_key_plain(int r, int h) {
   return 8 * (r / 4) + 4 * h + (r & 3);
 }
 
+// Head slots an XCD works on side by side (see block_coords).  Measured
+// on MI355X at B H = 32, T = 8192, causal (us per launch, one box): all four
+// of an XCD's heads interleaved 535.5, two at a time 536.3, one at a time
+// 549.4 (the heavy blocks of one head end together and leave CUs idle);
+// two at a time halves the number of heads whose K and V compete for an
+// XCD's L2 at no cost in time.
+constexpr int kHeadsInFlight = 2;
+
 // Workgroup id -> (query head bhq, key/value head bhkv, query block qb).
-// Heavy-first: the highest query blocks (most key tiles under a causal mask)
-// get the lowest ids.  Within a block index, ids walk the heads so that id
-// and id + BH*k fall on the same XCD whenever BH is a multiple of 8
-// (workgroups are dispatched round-robin over the 8 XCDs).  With grouped
-// key/value heads (G query heads per key/value head, "FlashAttention --
-// avoid writing the giant intermediate", the closing note on grouped-query
-// attention), head slot hid maps to member hid / NKV of group hid % NKV, so
-// the G query heads that read one key/value head also share an XCD and its
-// L2 whenever NKV = BH / G is a multiple of 8.  G = 1 is the identity.
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each
+// with its own L2.  When the head slots split evenly over the XCDs in
+// groups of kHeadsInFlight, XCD x takes its slots x, x + 8, ... in groups
+// of kHeadsInFlight, each group's query blocks heavy-first (the highest
+// blocks, most key tiles under a causal mask, first) with the group's
+// heads alternating; otherwise ids walk all heads within each block index,
+// heavy-first.  Either way all blocks of one head run on one XCD and share
+// its L2.  With grouped key/value heads (G query heads per key/value head,
+// "FlashAttention -- avoid writing the giant intermediate", the closing note
+// on grouped-query attention), head slot hid maps to member hid / NKV of
+// group hid % NKV, so the G query heads that read one key/value head also
+// share an XCD whenever NKV = BH / G is a multiple of 8.  G = 1 is the
+// identity.
 __device__ __forceinline__ void block_coords(int BH, int nqb, int G, int& bhq, int& bhkv,
                                              int& qb) {
   const int id = blockIdx.x;
-  qb = nqb - 1 - id / BH;
-  const int hid = id % BH;
+  int hid;
+  if (BH % (8 * kHeadsInFlight) == 0) {
+    const int r = id / 8, s = r % (kHeadsInFlight * nqb);
+    qb = nqb - 1 - s / kHeadsInFlight;
+    hid = id % 8 + 8 * (kHeadsInFlight * (r / (kHeadsInFlight * nqb)) + s % kHeadsInFlight);
+  } else {
+    qb = nqb - 1 - id / BH;
+    hid = id % BH;
+  }
   const int nkv = BH / G;
   bhkv = hid % nkv;
   bhq = bhkv * G + hid / nkv;
