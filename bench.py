@@ -328,8 +328,13 @@ def mfma_ceiling(dev, sampler=None, shape: int = 0):
 
 
 def launch_spread(per):
-    """First and last five launch durations (ms) of the timed region."""
-    return {"first5_ms": [round(x, 4) for x in per[:5]],
+    """Median and the first and last five launch durations (ms) of the
+    timed region."""
+    srt = sorted(per)
+    mid = len(srt) // 2
+    median = srt[mid] if len(srt) % 2 else 0.5 * (srt[mid - 1] + srt[mid])
+    return {"median_launch_ms": round(median, 4),
+            "first5_ms": [round(x, 4) for x in per[:5]],
             "last5_ms": [round(x, 4) for x in per[-5:]]}
 
 
@@ -763,6 +768,11 @@ def main() -> int:
               "T": T, "d": d,
               "causal": causal, "scale": scale, "qk_mult": w.get("qk_mult", 1.0),
               "flops_per_step": fl, "kernel": kname, "parallelism": "single GPU"}
+    if causal:
+        # the metric counts 4 T^2 d per head halved; the causal mask keeps
+        # T (T + 1) / 2 score entries, the diagonal included
+        config["flops_exact_causal"] = (4.0 * B * H * d * T * (T + 1) / 2
+                                        * (2.5 if bwd else 1.0))
     if bwd:
         config["kernels"] = knames
         config["dout_seed"] = x.seed + DOUT_SEED_OFFSET

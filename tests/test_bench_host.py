@@ -39,9 +39,11 @@ def test_sampler_reports_its_error():
 
 
 def test_launch_spread_and_blas_info():
-    per = [1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0]
-    assert bench.launch_spread(per) == {"first5_ms": [1.0, 2.0, 3.0, 4.0, 5.0],
-                                        "last5_ms": [3.0, 4.0, 5.0, 6.0, 7.0]}
+    per = [1.0, 2.0, 7.0, 4.0, 5.0, 6.0, 3.0]
+    assert bench.launch_spread(per) == {"median_launch_ms": 4.0,
+                                        "first5_ms": [1.0, 2.0, 7.0, 4.0, 5.0],
+                                        "last5_ms": [7.0, 4.0, 5.0, 6.0, 3.0]}
+    assert bench.launch_spread([1.0, 3.0])["median_launch_ms"] == 2.0
     info = bench.blas_info()
     assert isinstance(info, list)
 
