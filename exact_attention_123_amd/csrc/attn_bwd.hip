@@ -14,12 +14,13 @@
 // either.
 //
 // Three kernels, in stream order:
-//   1. prep : Delta_i = sum_c dO_ic O_ic and LSE_i * log2(e) per query row,
-//             into the caller's workspace.
-//   2. dkdv : one workgroup per 128 keys of a head (32 per wave), K and V of
-//             those keys held in registers; it walks 64-query tiles of Q and
-//             dO (staged in LDS) and accumulates dV^T += dO^T P and
-//             dK^T += Q^T dS in registers.
+//   1. prep : -Delta_i = -sum_c dO_ic O_ic and the log-sum-exp (as -LSE_i /
+//             scale, or -LSE_i log2(e)) per query row, into the caller's
+//             workspace.
+//   2. dkdv : one workgroup of 8 waves per 256 keys of a head (32 per
+//             wave), K of those keys staged in LDS and V held in registers;
+//             it walks 64-query tiles of Q and dO (staged in LDS) and
+//             accumulates dV^T += dO^T P and dK^T += Q^T dS in registers.
 //   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
 //             registers; it walks 64-key tiles of K and V (staged in LDS)
 //             and accumulates dQ^T += K^T dS^T.
@@ -46,7 +47,9 @@ using namespace attn_tiles;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
-constexpr int kBK = 128;       // keys per dkdv workgroup
+constexpr int kDkdvWaves = 8;  // dkdv: 8 waves, 256 keys per workgroup
+constexpr int kDkdvThreads = 64 * kDkdvWaves;
+constexpr int kBK = 256;       // keys per dkdv workgroup
 constexpr int kBQ = 128;       // queries per dq workgroup
 constexpr int kTile = 64;      // rows of a staged Q/dO (dkdv) or K/V (dq) tile
 // Heads an XCD works on side by side in the dkdv and dq kernels (see their
@@ -62,13 +65,15 @@ struct BwdTile : RowTile<D> {
 };
 
 // ---------------------------------------------------------------------------
-// 1. prep: Delta_i = sum_c dO_ic O_ic (fp32) and LSE_i * log2(e), one row per
-// D / 8 lanes.  ws[0 .. n) = Delta, ws[n .. 2 n) = LSE * log2(e), n = B H T.
+// 1. prep: -Delta_i = -sum_c dO_ic O_ic (fp32) and the row's log-sum-exp in
+// the form the kernels start from, one row per D / 8 lanes.  ws[0 .. n) =
+// -Delta, ws[n .. 2 n) = -LSE / scale when the scale is folded into the
+// score accumulator (see the dK/dV kernel), else -LSE * log2(e); n = B H T.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(
     const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
-    float* __restrict__ ws, int64_t n) {
+    float* __restrict__ ws, int64_t n, float lse_mult) {
   constexpr int LPR = D / 8;  // lanes per row
   const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
   const int sub = threadIdx.x % LPR;
@@ -82,16 +87,30 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
   if (row < n && sub == 0) {
-    ws[row] = acc;
-    ws[n + row] = LSE[row] * kLog2e;
+    ws[row] = -acc;
+    ws[n + row] = LSE[row] * lse_mult;
   }
 }
 
 // ---------------------------------------------------------------------------
 // 2. dkdv
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
+// FOLD: the score accumulator starts from -LSE_i / scale, so that the
+// exponent c (S_ij + v_i) = scale log2(e) S_ij - LSE_i log2(e) needs one
+// multiply per element and no per-element row statistic beside the
+// accumulator (the dP accumulator likewise starts from -Delta_i).  Used for
+// |scale| >= 2^-32, where -LSE / scale is finite; otherwise (scale 0
+// included) the exponent is fma(S_ij, c, -LSE_i log2(e)) on a zero-started
+// accumulator.  The fp32 error of the folded exponent is about 2^-24
+// |LSE log2(e)|, against 2^-9 for the bf16 rounding of P that follows.
+//
+// Eight waves, two per SIMD (at most 256 registers per lane, so that the
+// matrix results stay in VGPRs where the softmax reads them): the block's
+// 256 keys are staged in LDS once, each wave holds V of its 32 keys and
+// its dK, dV accumulators in registers, and the staged Q and dO tiles serve
+// all 256 keys.
+template <int D, bool CAUSAL, bool FOLD>
+__global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
     __bf16* __restrict__ dV, int T, int BHkv, int G, int nkb, float c, float scale) {
@@ -100,15 +119,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
 
   // Two stages, each operand and stage its own object: the compiler then
   // tells the direct-to-LDS loads into one stage from the reads of the
-  // other and does not wait for the loads in flight before reading.
-  __shared__ __attribute__((aligned(1024))) char sQ0[C::TBYTES];
-  __shared__ __attribute__((aligned(1024))) char sQ1[C::TBYTES];
-  __shared__ __attribute__((aligned(1024))) char sG0[C::TBYTES];  // dO
-  __shared__ __attribute__((aligned(1024))) char sG1[C::TBYTES];
-  __shared__ __attribute__((aligned(16))) float sL0[kTile];       // LSE * log2(e)
+  // other and does not wait for the loads in flight before reading.  The
+  // stages must lie below 64 KiB, where their fixed offsets fit the LDS
+  // instructions' immediate field: aligned to their own size, they are laid
+  // out ahead of the block's keys (the layout orders by alignment) at no
+  // cost in padding.
+  __shared__ __attribute__((aligned(C::TBYTES))) char sQ0[C::TBYTES];
+  __shared__ __attribute__((aligned(C::TBYTES))) char sQ1[C::TBYTES];
+  __shared__ __attribute__((aligned(C::TBYTES))) char sG0[C::TBYTES];  // dO
+  __shared__ __attribute__((aligned(C::TBYTES))) char sG1[C::TBYTES];
+  __shared__ __attribute__((aligned(16))) float sL0[kTile];       // LSE statistic
   __shared__ __attribute__((aligned(16))) float sL1[kTile];
-  __shared__ __attribute__((aligned(16))) float sD0[kTile];       // Delta
+  __shared__ __attribute__((aligned(16))) float sD0[kTile];       // -Delta
   __shared__ __attribute__((aligned(16))) float sD1[kTile];
+  __shared__ __attribute__((aligned(1024))) char sK[kBK * RB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -133,28 +157,41 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
     bhkv = id % BHkv;
   }
   const size_t head = (size_t)bhkv * (size_t)T * D;
-  const int k0 = kb * kBK, kw0 = k0 + 32 * wave;
+  // Waves w and w + 4 share a SIMD; they take key groups w and 7 - w, so
+  // that under a causal mask every SIMD skips the same number of sub-tiles
+  // on the diagonal.
+  const int kg = wave < 4 ? wave : 11 - wave;
+  const int k0 = kb * kBK, kw0 = k0 + 32 * kg;
   const int64_t n = (int64_t)BHkv * G * T;
 
-  // K and V of the wave's 32 keys: B operands [d][key] of S = Q K^T and
-  // dP = dO V^T; lane (j, h) holds row kw0 + j, d = 16 s + 8 h .. + 8.
-  bf16x8_t kf[NDS], vf[NDS];
+  // The block's keys, rows k0 .. k0 + 255 (rows >= T read as zero).
   {
-    const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + head, T * RB);
+    TileDma<D, kBK, kDkdvWaves> kdma;
+    kdma.init(wave, lane);
+    kdma.load(sK, K + head, T, k0, wave);
+  }
+  // V of the wave's 32 keys: B operand [d][key] of dP = dO V^T; lane (j, h)
+  // holds row kw0 + j, d = 16 s + 8 h .. + 8.
+  bf16x8_t vf[NDS];
+  {
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + head, T * RB);
 #pragma unroll
-    for (int s = 0; s < NDS; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rK, (kw0 + j) * RB + (16 * s + 8 * h) * 2));
+    for (int s = 0; s < NDS; ++s)
       vf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rV, (kw0 + j) * RB + (16 * s + 8 * h) * 2));
-    }
   }
+  // K of the same keys from LDS, as the B operand [d][key] of S = Q K^T:
+  // lane (j, h) reads row 32 kg + j, chunk 2 s + h (swizzled).
+  const char* tk = sK + 32 * kg * RB;
+  int kaddr[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) kaddr[s] = j * RB + 16 * ((2 * s + h) ^ swz<D>(j));
 
   TileAddr<D> ad;
   ad.init(lane);
-  TileDma<D, kTile, kWaves> dma;
+  TileDma<D, kTile, kDkdvWaves> dma;
   dma.init(wave, lane);
   // Query tile `qt` of member `m` of the group (query head bhkv G + m).
-  // Row statistics: one dword per lane of wave 0 (L) and wave 1 (Delta),
+  // Row statistics: one dword per lane of wave 0 (LSE) and wave 1 (-Delta),
   // lane L landing at 4 L; rows >= T read as zero.
   auto stage = [&](char* tq, char* tg, float* tl, float* td, int m, int qt)
       __attribute__((always_inline)) {
@@ -199,32 +236,53 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
       // Nothing to add when every query of the sub-tile precedes every key
       // of the wave (causal) or lies past the end of the sequence (its Q
       // and dO rows read as zero).  Without a branch here the non-causal
-      // kernels need up to 512 registers per lane and spill.
+      // kernels need more registers than they have and spill.
       if (CAUSAL ? i0 + 31 < kw0 : i0 >= T) continue;
-      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
-#pragma unroll
-      for (int s = 0; s < NDS; ++s) {
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tq, 32 * u * RB + ad.row[s]), kf[s],
-                                                    S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tg, 32 * u * RB + ad.row[s]), vf[s],
-                                                     dP, 0, 0, 0);
-      }
       // Register 8 a + e of lane (j, h) holds query i0 + 16 a + 8 h + e and
-      // key kw0 + j.
-      float p[16], g[16];
+      // key kw0 + j.  The accumulators start from the row statistics: dP
+      // from -Delta, S from -LSE / scale (FOLD) or zero.
+      f32x16_t S, dP;
+      float p[16];
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int q8 = 32 * u + 16 * a + 8 * h;
-        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(&tl[q8]);
-        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&tl[q8 + 4]);
         const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(&td[q8]);
         const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(&td[q8 + 4]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lse2 = e < 4 ? l0[e] : l1[e - 4];
-          const float dl = e < 4 ? d0[e] : d1[e - 4];
-          p[8 * a + e] = exp2_hw(fmaf(S[8 * a + e], c, -lse2));
-          g[8 * a + e] = dP[8 * a + e] - dl;
+        for (int e = 0; e < 4; ++e) {
+          dP[8 * a + e] = d0[e];
+          dP[8 * a + 4 + e] = d1[e];
+        }
+        if constexpr (FOLD) {
+          const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(&tl[q8]);
+          const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&tl[q8 + 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            S[8 * a + e] = l0[e];
+            S[8 * a + 4 + e] = l1[e];
+          }
+        }
+      }
+      if constexpr (!FOLD) S = f32x16_t{};
+#pragma unroll
+      for (int s = 0; s < NDS; ++s) {
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tq, 32 * u * RB + ad.row[s]),
+                                                    lds_row(tk, kaddr[s]), S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tg, 32 * u * RB + ad.row[s]), vf[s],
+                                                     dP, 0, 0, 0);
+      }
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = exp2_hw(S[r] * c);
+      } else {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int q8 = 32 * u + 16 * a + 8 * h;
+          const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(&tl[q8]);
+          const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(&tl[q8 + 4]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            p[8 * a + e] = exp2_hw(fmaf(S[8 * a + e], c, e < 4 ? l0[e] : l1[e - 4]));
         }
       }
       // The mask (keys past the end of the sequence, and causal keys after
@@ -246,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           pb[a][e] = (__bf16)p[8 * a + e];
-          db[a][e] = (__bf16)(p[8 * a + e] * g[8 * a + e]);
+          db[a][e] = (__bf16)(p[8 * a + e] * dP[8 * a + e]);
         }
       // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 queries.
 #pragma unroll
@@ -297,7 +355,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int T,
-    int BH, int nqb, int G, float c, float scale) {
+    int BH, int nqb, int G, float c, float cw, float scale) {
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
 
@@ -346,8 +404,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       gf[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rG, qg * RB + (16 * s + 8 * h) * 2));
     }
   }
-  const float dl = qg < T ? ws[(size_t)bh * T + qg] : 0.0f;
-  const float lse2 = qg < T ? ws[n + (size_t)bh * T + qg] : 0.0f;
+  // -Delta and -LSE log2(e) of the lane's query (cw: the factor that turns
+  // the workspace's form of the log-sum-exp into the latter)
+  const float nd = qg < T ? ws[(size_t)bh * T + qg] : 0.0f;
+  const float nl = qg < T ? cw * ws[n + (size_t)bh * T + qg] : 0.0f;
 
   TileAddr<D> ad;
   ad.init(lane);
@@ -383,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       // query qg.
       float p[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(S[r], c, -lse2));
+      for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(S[r], c, nl));
       // The mask only on sub-tiles that need it (a branch, as in the dK/dV
       // kernel): key kv0 + 16 a + 8 h + e is masked iff 16 a + e >= lim.
       if ((CAUSAL && kv0 + 31 > qw0) || kv0 + 31 >= T) {
@@ -397,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) db[a][e] = (__bf16)(p[8 * a + e] * (dP[8 * a + e] - dl));
+        for (int e = 0; e < 8; ++e) db[a][e] = (__bf16)(p[8 * a + e] * (dP[8 * a + e] + nd));
       // dQ^T += K^T dS^T over the sub-tile's 32 keys.
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
@@ -450,10 +510,14 @@ attn_status check_device() {
   return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
-template <int D>
+template <int D, bool FOLD>
 const void* dkdv_kernel(int causal) {
-  return causal ? (const void*)attn_bwd_dkdv_kernel<D, true>
-                : (const void*)attn_bwd_dkdv_kernel<D, false>;
+  return causal ? (const void*)attn_bwd_dkdv_kernel<D, true, FOLD>
+                : (const void*)attn_bwd_dkdv_kernel<D, false, FOLD>;
+}
+template <int D>
+const void* dkdv_kernel(int causal, bool fold) {
+  return fold ? dkdv_kernel<D, true>(causal) : dkdv_kernel<D, false>(causal);
 }
 template <int D>
 const void* dq_kernel(int causal) {
@@ -503,12 +567,18 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
   const int t = (int)T, bh = (int)BH, bhkv = (int)BHkv, g = (int)(H / H_kv);
   const int64_t n = BH * T;
   const float c = scale * kLog2e;
+  // Fold the scale into the dK/dV kernel's score accumulator where
+  // -LSE / scale stays finite (see attn_bwd_dkdv_kernel).
+  const bool fold = std::fabs(scale) >= 0x1p-32f;
+  const float lse_mult = fold ? -1.0f / scale : -kLog2e;
+  const float cw = fold ? c : 1.0f;
   {
     const int rows_per_block = kThreads / (int)(d / 8);
     const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block));
     const __bf16* ob = (const __bf16*)o;
     const __bf16* gb = (const __bf16*)dout;
-    void* args[] = {(void*)&ob, (void*)&gb, (void*)&lse, (void*)&ws, (void*)&n};
+    void* args[] = {(void*)&ob, (void*)&gb, (void*)&lse, (void*)&ws, (void*)&n,
+                    (void*)&lse_mult};
     const void* kern = d == 64 ? (const void*)attn_bwd_prep_kernel<64>
                                : (const void*)attn_bwd_prep_kernel<128>;
     if (hipLaunchKernel(kern, grid, dim3(kThreads), args, 0, stream) != hipSuccess)
@@ -523,8 +593,9 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     void* args[] = {(void*)&qb,  (void*)&kb_, (void*)&vb, (void*)&gb,  (void*)&wsc,
                     (void*)&dkb, (void*)&dvb, (void*)&t,  (void*)&bhkv, (void*)&g,
                     (void*)&nkb, (void*)&c,   (void*)&scale};
-    const void* kern = d == 64 ? dkdv_kernel<64>(causal) : dkdv_kernel<128>(causal);
-    if (hipLaunchKernel(kern, dim3((unsigned)(bhkv * nkb)), dim3(kThreads), args, 0, stream) !=
+    const void* kern = d == 64 ? dkdv_kernel<64>(causal, fold) : dkdv_kernel<128>(causal, fold);
+    if (hipLaunchKernel(kern, dim3((unsigned)(bhkv * nkb)), dim3(kDkdvThreads), args, 0,
+                        stream) !=
         hipSuccess)
       return ATTN_ERR_LAUNCH;
   }
@@ -533,7 +604,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     __bf16* dqb = (__bf16*)dq;
     void* args[] = {(void*)&qb, (void*)&kb_, (void*)&vb,  (void*)&gb, (void*)&wsc,
                     (void*)&dqb, (void*)&t,  (void*)&bh,  (void*)&nqb, (void*)&g,
-                    (void*)&c,  (void*)&scale};
+                    (void*)&c,  (void*)&cw, (void*)&scale};
     const void* kern = d == 64 ? dq_kernel<64>(causal) : dq_kernel<128>(causal);
     if (hipLaunchKernel(kern, dim3((unsigned)(bh * nqb)), dim3(kThreads), args, 0, stream) !=
         hipSuccess)
@@ -554,13 +625,13 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which) {
   if ((d != 64 && d != 128) || (causal != 0 && causal != 1) || which < 0 || which > 2)
     return nullptr;
   static const char* names[2][2][3] = {
-      {{"attn_bwd_prep_d64", "attn_bwd_dkdv_bf16_d64_full_bk128_bq64_w4",
+      {{"attn_bwd_prep_d64", "attn_bwd_dkdv_bf16_d64_full_bk256_bq64_w8",
         "attn_bwd_dq_bf16_d64_full_bq128_bk64_w4"},
-       {"attn_bwd_prep_d64", "attn_bwd_dkdv_bf16_d64_causal_bk128_bq64_w4",
+       {"attn_bwd_prep_d64", "attn_bwd_dkdv_bf16_d64_causal_bk256_bq64_w8",
         "attn_bwd_dq_bf16_d64_causal_bq128_bk64_w4"}},
-      {{"attn_bwd_prep_d128", "attn_bwd_dkdv_bf16_d128_full_bk128_bq64_w4",
+      {{"attn_bwd_prep_d128", "attn_bwd_dkdv_bf16_d128_full_bk256_bq64_w8",
         "attn_bwd_dq_bf16_d128_full_bq128_bk64_w4"},
-       {"attn_bwd_prep_d128", "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4",
+       {"attn_bwd_prep_d128", "attn_bwd_dkdv_bf16_d128_causal_bk256_bq64_w8",
         "attn_bwd_dq_bf16_d128_causal_bq128_bk64_w4"}}};
   return names[d == 128 ? 1 : 0][causal][which];
 }

@@ -135,8 +135,10 @@ attn_status attn_fwd_f32(const float* q, const float* k, const float* v,
  *   lse:   const float [B][H][T];
  *   dq, dk, dv: __hip_bfloat16 [B][H][T][d], written (nearest-even);
  *   ws:    float workspace of 2*B*H*T elements, owned by the caller.  On
- *          return ws[0 .. B*H*T) holds Delta and ws[B*H*T .. 2*B*H*T) holds
- *          lse * log2(e), both [B][H][T].
+ *          return ws[0 .. B*H*T) holds -Delta and ws[B*H*T .. 2*B*H*T)
+ *          holds -lse / scale when |scale| >= 2^-32, else -lse * log2(e),
+ *          both [B][H][T] (the values the kernels start their score and dP
+ *          accumulators from).
  *   B, H, T, d, causal, scale: as for attn_fwd.
  * S, P, dP, dS, Delta are fp32; P and dS are rounded to bf16 (nearest-even)
  * as inputs of the bf16 MFMA contractions, which accumulate in fp32.  Three
@@ -165,7 +167,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v,
 /*
  * Name of kernel `which` (0 = row statistics, 1 = dK/dV, 2 = dQ) that
  * attn_bwd launches for head dimension d and the causal flag, e.g.
- * "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4".  NULL if unsupported.
+ * "attn_bwd_dkdv_bf16_d128_causal_bk256_bq64_w8".  NULL if unsupported.
  */
 const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
 

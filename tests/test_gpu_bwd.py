@@ -114,11 +114,12 @@ def check_head(x, do_bits, b, h, res, causal, scale, rows=None, keys=None, ub=U)
                                  f"{want[i]:.6g} tol {tol[i]:.3g}")
         worst = max(worst, float(ratio.max()))
     n = B * H * T
-    delta = ws[:n].reshape(B, H, T)[b, h][r]
+    # the workspace: -Delta, and -LSE / scale (-LSE log2(e) for |scale| < 2^-32)
+    delta = -ws[:n].reshape(B, H, T)[b, h][r]
     assert np.all(np.abs(delta - ref["Delta"]) <= ub * bnd[r] + 1e-6), "Delta"
-    lse2 = ws[n:].reshape(B, H, T)[b, h][r]
-    assert np.all(np.abs(lse2 - ref["LSE"][r] * math.log2(math.e))
-                  <= 1e-5 * (1 + np.abs(ref["LSE"][r]))), "LSE * log2(e)"
+    stat = ws[n:].reshape(B, H, T)[b, h][r]
+    want = -ref["LSE"][r] / scale if abs(scale) >= 2.0 ** -32 else -ref["LSE"][r] * math.log2(math.e)
+    assert np.all(np.abs(stat - want) <= 1e-5 * (1 + np.abs(want))), "LSE statistic"
     return worst
 
 
@@ -143,10 +144,14 @@ def test_bwd_ragged(T, causal, d):
         check_head(x, do, 0, h, res, causal, scale)
 
 
-@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.5, 1.0])
-def test_bwd_other_scales(scale):
-    say(f"[bwd scale] {scale}")
-    B, H, T, d = 1, 2, 300, 64
+# 1e-12 and 0 take the kernels' unfolded exponent (|scale| < 2^-32), the
+# others the folded one (score accumulator started from -LSE / scale; at
+# 2^-31 that start value is about 1e10)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 1e-12, 2.0 ** -31, 0.5, 1.0])
+def test_bwd_other_scales(scale, d):
+    say(f"[bwd scale] {scale} d={d}")
+    B, H, T = 1, 2, 300
     x = make_qkv(B, H, T, d, seed=5000)
     do = make_dout(B, H, T, d, seed=5001)
     for causal in (True, False):
