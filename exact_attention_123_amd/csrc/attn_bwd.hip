@@ -408,6 +408,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   // the workspace's form of the log-sum-exp into the latter)
   const float nd = qg < T ? ws[(size_t)bh * T + qg] : 0.0f;
   const float nl = qg < T ? cw * ws[n + (size_t)bh * T + qg] : 0.0f;
+  // Every dP^T accumulator starts from -Delta of the lane's query, so that
+  // dP - Delta comes out of the contraction (16 registers held throughout;
+  // the non-causal d = 128 kernel has none to spare and subtracts instead).
+  constexpr bool kFoldDelta = CAUSAL || D == 64;
+  f32x16_t dP0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dP0[r] = kFoldDelta ? nd : 0.0f;
 
   TileAddr<D> ad;
   ad.init(lane);
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       const int kv0 = t * kTile + 32 * u;
       // every key of the sub-tile follows every query of the wave
       if (CAUSAL && kv0 > qw0 + 31) continue;
-      f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+      f32x16_t S = f32x16_t{}, dP = dP0;
 #pragma unroll
       for (int s = 0; s < NDS; ++s) {
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tk, 32 * u * RB + ad.row[s]), qf[s],
@@ -457,7 +464,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) db[a][e] = (__bf16)(p[8 * a + e] * (dP[8 * a + e] + nd));
+        for (int e = 0; e < 8; ++e)
+          db[a][e] = (__bf16)(p[8 * a + e] * (kFoldDelta ? dP[8 * a + e] : dP[8 * a + e] + nd));
       // dQ^T += K^T dS^T over the sub-tile's 32 keys.
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
