@@ -148,10 +148,12 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(
   // key block.
   const int id = blockIdx.x;
   int kb, bhkv;
-  if (BHkv % (8 * kHeadsInFlight) == 0) {
-    const int r = id / 8, s = r % (kHeadsInFlight * nkb);
-    kb = s / kHeadsInFlight;
-    bhkv = id % 8 + 8 * (kHeadsInFlight * (r / (kHeadsInFlight * nkb)) + s % kHeadsInFlight);
+  bool up = false;
+  if (BHkv % 8 == 0) {
+    const int r = id / 8;
+    kb = r % nkb;
+    bhkv = id % 8 + 8 * (r / nkb);
+    up = (r / nkb) & 1;
   } else {
     kb = id / BHkv;
     bhkv = id % BHkv;
@@ -225,7 +227,9 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(
   const int nqt = (T + kTile - 1) / kTile;
   const int per = nqt - qt0;  // > 0: k0 < T
   const int nit = G * per;
-  auto qt_of = [&](int it) __attribute__((always_inline)) { return nqt - 1 - it % per; };
+  auto qt_of = [&](int it) __attribute__((always_inline)) {
+    return up ? qt0 + it % per : nqt - 1 - it % per;
+  };
   // Query tile number `it` of the walk, staged in (tq, tg, tl, td).
   auto tile = [&](const char* tq, const char* tg, const float* tl, const float* td, int it)
       __attribute__((always_inline)) {
