@@ -255,9 +255,13 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
 
   // LDS: three K and three V stages, separate objects so that the compiler
   // can tell the direct-to-LDS writes into one stage from reads of another.
-  __shared__ __attribute__((aligned(1024))) char sK0[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[C::KBYTES];
-  __shared__ __attribute__((aligned(1024))) char sK2[C::KBYTES];
+  // The K stages, aligned to their size (no padding), are laid out first
+  // (the layout orders by alignment), then the V stages: at d = 128 the
+  // second and third V stages start at 64 and 80 KiB, past the 16-bit
+  // immediate offset of the LDS instructions (see vhi below).
+  __shared__ __attribute__((aligned(C::KBYTES))) char sK0[C::KBYTES];
+  __shared__ __attribute__((aligned(C::KBYTES))) char sK1[C::KBYTES];
+  __shared__ __attribute__((aligned(C::KBYTES))) char sK2[C::KBYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[C::VBYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[C::VBYTES];
   __shared__ __attribute__((aligned(1024))) char sV2[C::VBYTES];
@@ -404,6 +408,16 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) vaddr[dt] = vaddr0 ^ (64 * dt);
   }
+  // For the V stages at 64 KiB and beyond: the same addresses plus 64 KiB,
+  // kept opaque, so that a read of such a stage is one register plus an
+  // immediate (the stage's offset past 64 KiB); the compiler would otherwise
+  // fold the 64 KiB back into the offset and add it on every read.
+  int vhi[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    vhi[dt] = vaddr[dt] + 65536;
+    asm volatile("" : "+v"(vhi[dt]));
+  }
 
   f32x16_t oacc[NDT];
 #pragma unroll
@@ -425,13 +439,16 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
     }
   };
 
-  // O^T += V^T P^T for the 32-key half `half` of the V tile in `vb`.
-  auto pv = [&](const char* vb, int half, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+  // O^T += V^T P^T for the 32-key half `half` of the V tile in `vb`; HI:
+  // the stage lies at 64 KiB or beyond (the address is still formed from the
+  // stage, so that the compiler knows which stage a read touches).
+  auto pv = [&](auto hi, const char* vb, int half, const bf16x8_t (&pb)[2])
+                __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const char* base = vb + vaddr[dt];
+        const char* base = decltype(hi)::value ? vb + (vhi[dt] - 65536) : vb + vaddr[dt];
         const int off = (32 * half + 16 * a) * RB;
         const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(base + off));
         const i16x4_t hi =
@@ -565,7 +582,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   // One sub-step for score sub-tile k: S_k is in scur, P_{k-1} in pprev;
   // computes S_{k+1} from K half kh of kb and accumulates P_{k-1} V_{k-1}
   // from V half vh of vb.
-  auto substep = [&](auto has_pv, const char* kb, int kh, const char* vb, int vh, f32x16_t& scur,
+  auto substep = [&](auto has_pv, auto vhi_stage, const char* kb, int kh, const char* vb, int vh,
+                     f32x16_t& scur,
                      f32x16_t& snext, const bf16x8_t(&pprev)[2], bf16x8_t(&pcur)[2],
                      int k) __attribute__((always_inline)) {
     if constexpr (PRESCALE) {
@@ -576,7 +594,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
     qk(kb, kh, snext);
     float ls, ws;
     if constexpr (decltype(has_pv)::value) {
-      pv(vb, vh, pprev);
+      pv(vhi_stage, vb, vh, pprev);
       const bool over = softmax(scur, pcur, ls, ws);
       interleave();
       if (over) regrow(std::false_type{}, scur, pcur, ls, ws);
@@ -594,6 +612,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   // loads of the previous iteration (K_{tau+2}, V_{tau+1}) must have landed.
   auto iteration = [&](auto stage, int tau) __attribute__((always_inline)) {
     constexpr int R = decltype(stage)::value;  // tau % 3
+    // V stage R (laid out after the three K stages) past 64 KiB?
+    using VHi = std::integral_constant<bool, 3 * C::KBYTES + R * C::VBYTES >= 65536>;
     char* kcur = R == 0 ? sK1 : R == 1 ? sK2 : sK0;
     char* kfree = R == 0 ? sK0 : R == 1 ? sK1 : sK2;
     char* vcur = R == 0 ? sV0 : R == 1 ? sV1 : sV2;
@@ -602,8 +622,8 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
     dma_v(vfree, tau + 2);
     ATTN_DEBUG_SYNC();
     if (tau < tskip) {
-      substep(std::true_type{}, kcur, 0, vcur, 0, sY, sX, pX, pY, 2 * tau + 1);
-      substep(std::true_type{}, kcur, 1, vcur, 1, sX, sY, pY, pX, 2 * tau + 2);
+      substep(std::true_type{}, VHi{}, kcur, 0, vcur, 0, sY, sX, pX, pY, 2 * tau + 1);
+      substep(std::true_type{}, VHi{}, kcur, 1, vcur, 1, sX, sY, pY, pX, 2 * tau + 2);
     }
     ATTN_DEBUG_SYNC();
     // Every wave issued KPER + VPER loads this iteration: waiting down to
@@ -624,7 +644,7 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void attn_fwd_bf16_kernel(
   wait_dma(std::integral_constant<int, 0>{});
   __syncthreads();
   qk(sK0, 0, sX);
-  substep(std::false_type{}, sK0, 1, sV0, 0, sX, sY, pY, pX, 0);
+  substep(std::false_type{}, std::false_type{}, sK0, 1, sV0, 0, sX, sY, pY, pX, 0);
   // K_0's stage receives K_3 in iteration 0: every wave must be done
   // reading it first.
   __syncthreads();
