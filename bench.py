@@ -679,8 +679,9 @@ def main() -> int:
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
         ws = torch.empty(2 * B * H * T, dtype=torch.float32, device=dev)
         ea.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
-        kname = ea.bwd_kernel_name(d, causal, 1)
-        knames = [ea.bwd_kernel_name(d, causal, i) for i in range(3)]
+        # the instances attn_bwd launches for these sizes on this device
+        kname = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 1)
+        knames = [ea.bwd_kernel_name_for(B, H, H, T, d, causal, i) for i in range(3)]
         fl = ea.bwd_flops(B, H, T, d, causal)
     else:
         do_bits = None

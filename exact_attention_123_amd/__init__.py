@@ -24,7 +24,7 @@ __all__ = [
     "decode_workspace_bytes", "decode_splits",
     "attn_fwd_materialized", "forward_materialized",
     "kernel_name", "fwd_kernel_name_for", "fwd_f32_kernel_name_for", "decode_kernel_name_for",
-    "bwd_kernel_name", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
+    "bwd_kernel_name", "bwd_kernel_name_for", "status_string", "AttnError", "LibraryNotBuilt", "load_library",
     "LIB_PATH", "STATUS", "flops", "bwd_flops",
 ]
 
@@ -61,6 +61,7 @@ EXPORTS = {
     "attn_fwd_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
     "attn_fwd_f32_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 4 + [ctypes.c_int]),
     "attn_bwd_kernel_name": (ctypes.c_char_p, [ctypes.c_int64, ctypes.c_int, ctypes.c_int]),
+    "attn_bwd_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 5 + [ctypes.c_int] * 2),
     "attn_decode_kernel_name_for": (ctypes.c_char_p, [ctypes.c_int64] * 6 + [ctypes.c_int]),
     # include/attn_probe.h
     "attn_probe_mfma": (ctypes.c_int, [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
@@ -142,6 +143,13 @@ def decode_kernel_name_for(B: int, H: int, H_kv: int, Tq: int, Tk: int, d: int, 
 def bwd_kernel_name(d: int, causal: bool, which: int):
     """Name of backward kernel ``which`` (0 row statistics, 1 dK/dV, 2 dQ)."""
     n = load_library().attn_bwd_kernel_name(int(d), int(bool(causal)), int(which))
+    return None if n is None else n.decode()
+
+
+def bwd_kernel_name_for(B: int, H: int, H_kv: int, T: int, d: int, causal: bool, which: int):
+    """Name of backward kernel ``which`` that attn_bwd_gqa launches for these
+    sizes on the current device (needs a GPU)."""
+    n = load_library().attn_bwd_kernel_name_for(B, H, H_kv, T, d, int(bool(causal)), int(which))
     return None if n is None else n.decode()
 
 

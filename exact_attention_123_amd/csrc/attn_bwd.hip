@@ -36,6 +36,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <atomic>
 #include <cstring>
 
 #include "attn.h"
@@ -47,9 +48,11 @@ using namespace attn_tiles;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
-constexpr int kDkdvWaves = 8;  // dkdv: 8 waves, 256 keys per workgroup
-constexpr int kDkdvThreads = 64 * kDkdvWaves;
-constexpr int kBK = 256;       // keys per dkdv workgroup
+// dkdv: 32 keys per wave; 8 waves (256 keys) per workgroup, or 4 waves
+// (128 keys) when the 256-key blocks would be fewer than the device's CUs
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvWavesSmall = 4;
+constexpr int kBK = 32 * kDkdvWaves;  // keys per dkdv workgroup (8 waves)
 constexpr int kBQ = 128;       // queries per dq workgroup
 constexpr int kTile = 64;      // rows of a staged Q/dO (dkdv) or K/V (dq) tile
 // Heads an XCD works on side by side in the dkdv and dq kernels (see their
@@ -104,18 +107,21 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(
 // accumulator.  The fp32 error of the folded exponent is about 2^-24
 // |LSE log2(e)|, against 2^-9 for the bf16 rounding of P that follows.
 //
-// Eight waves, two per SIMD (at most 256 registers per lane, so that the
+// NW = 8 waves, two per SIMD (at most 256 registers per lane, so that the
 // matrix results stay in VGPRs where the softmax reads them): the block's
 // 256 keys are staged in LDS once, each wave holds V of its 32 keys and
 // its dK, dV accumulators in registers, and the staged Q and dO tiles serve
-// all 256 keys.
-template <int D, bool CAUSAL, bool FOLD>
-__global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(
+// all 256 keys.  NW = 4 (128 keys, one wave per SIMD) for problems with
+// fewer 256-key blocks than CUs: there the heaviest block's walk over every
+// query tile sets the time, and a 128-key block halves it.
+template <int D, bool CAUSAL, bool FOLD, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
     __bf16* __restrict__ dV, int T, int BHkv, int G, int nkb, float c, float scale) {
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
+  constexpr int BK = 32 * NW;  // keys per workgroup
 
   // Two stages, each operand and stage its own object: the compiler then
   // tells the direct-to-LDS loads into one stage from the reads of the
@@ -132,7 +138,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float sL1[kTile];
   __shared__ __attribute__((aligned(16))) float sD0[kTile];       // -Delta
   __shared__ __attribute__((aligned(16))) float sD1[kTile];
-  __shared__ __attribute__((aligned(1024))) char sK[kBK * RB];
+  __shared__ __attribute__((aligned(1024))) char sK[BK * RB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,16 +165,16 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(
     bhkv = id % BHkv;
   }
   const size_t head = (size_t)bhkv * (size_t)T * D;
-  // Waves w and w + 4 share a SIMD; they take key groups w and 7 - w, so
-  // that under a causal mask every SIMD skips the same number of sub-tiles
-  // on the diagonal.
-  const int kg = wave < 4 ? wave : 11 - wave;
-  const int k0 = kb * kBK, kw0 = k0 + 32 * kg;
+  // With 8 waves, waves w and w + 4 share a SIMD; they take key groups w
+  // and 7 - w, so that under a causal mask every SIMD skips the same number
+  // of sub-tiles on the diagonal.
+  const int kg = NW == 8 ? (wave < 4 ? wave : 11 - wave) : wave;
+  const int k0 = kb * BK, kw0 = k0 + 32 * kg;
   const int64_t n = (int64_t)BHkv * G * T;
 
-  // The block's keys, rows k0 .. k0 + 255 (rows >= T read as zero).
+  // The block's keys, rows k0 .. k0 + BK - 1 (rows >= T read as zero).
   {
-    TileDma<D, kBK, kDkdvWaves> kdma;
+    TileDma<D, BK, NW> kdma;
     kdma.init(wave, lane);
     kdma.load(sK, K + head, T, k0, wave);
   }
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(
 
   TileAddr<D> ad;
   ad.init(lane);
-  TileDma<D, kTile, kDkdvWaves> dma;
+  TileDma<D, kTile, NW> dma;
   dma.init(wave, lane);
   // Query tile `qt` of member `m` of the group (query head bhkv G + m).
   // Row statistics: one dword per lane of wave 0 (LSE) and wave 1 (-Delta),
@@ -522,14 +528,40 @@ attn_status check_device() {
   return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
-template <int D, bool FOLD>
+template <int D, bool FOLD, int NW>
 const void* dkdv_kernel(int causal) {
-  return causal ? (const void*)attn_bwd_dkdv_kernel<D, true, FOLD>
-                : (const void*)attn_bwd_dkdv_kernel<D, false, FOLD>;
+  return causal ? (const void*)attn_bwd_dkdv_kernel<D, true, FOLD, NW>
+                : (const void*)attn_bwd_dkdv_kernel<D, false, FOLD, NW>;
+}
+template <int D, int NW>
+const void* dkdv_kernel(int causal, bool fold) {
+  return fold ? dkdv_kernel<D, true, NW>(causal) : dkdv_kernel<D, false, NW>(causal);
 }
 template <int D>
-const void* dkdv_kernel(int causal, bool fold) {
-  return fold ? dkdv_kernel<D, true>(causal) : dkdv_kernel<D, false>(causal);
+const void* dkdv_kernel(int causal, bool fold, int nw) {
+  return nw == kDkdvWavesSmall ? dkdv_kernel<D, kDkdvWavesSmall>(causal, fold)
+                               : dkdv_kernel<D, kDkdvWaves>(causal, fold);
+}
+
+// Compute units of the current device (cached per device; 256 if unknown).
+std::atomic<int> g_cus[64];
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return 256;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Waves per dK/dV workgroup for these sizes: 4 when the 256-key blocks of
+// all key/value heads are fewer than the CUs, else 8.
+int dkdv_waves(int64_t BHkv, int64_t T) {
+  return BHkv * ((T + kBK - 1) / kBK) < device_cus() ? kDkdvWavesSmall : kDkdvWaves;
 }
 template <int D>
 const void* dq_kernel(int causal) {
@@ -600,13 +632,15 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
                *gb = (const __bf16*)dout;
   const float* wsc = ws;
   {
-    int nkb = (int)((T + kBK - 1) / kBK);
+    const int nw = dkdv_waves(BHkv, T);
+    int nkb = (int)((T + 32 * nw - 1) / (32 * nw));
     __bf16 *dkb = (__bf16*)dk, *dvb = (__bf16*)dv;
     void* args[] = {(void*)&qb,  (void*)&kb_, (void*)&vb, (void*)&gb,  (void*)&wsc,
                     (void*)&dkb, (void*)&dvb, (void*)&t,  (void*)&bhkv, (void*)&g,
                     (void*)&nkb, (void*)&c,   (void*)&scale};
-    const void* kern = d == 64 ? dkdv_kernel<64>(causal, fold) : dkdv_kernel<128>(causal, fold);
-    if (hipLaunchKernel(kern, dim3((unsigned)(bhkv * nkb)), dim3(kDkdvThreads), args, 0,
+    const void* kern =
+        d == 64 ? dkdv_kernel<64>(causal, fold, nw) : dkdv_kernel<128>(causal, fold, nw);
+    if (hipLaunchKernel(kern, dim3((unsigned)(bhkv * nkb)), dim3(64 * nw), args, 0,
                         stream) !=
         hipSuccess)
       return ATTN_ERR_LAUNCH;
@@ -646,6 +680,19 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which) {
        {"attn_bwd_prep_d128", "attn_bwd_dkdv_bf16_d128_causal_bk256_bq64_w8",
         "attn_bwd_dq_bf16_d128_causal_bq128_bk64_w4"}}};
   return names[d == 128 ? 1 : 0][causal][which];
+}
+
+const char* attn_bwd_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t T, int64_t d,
+                                     int causal, int which) {
+  if (B <= 0 || H <= 0 || H_kv <= 0 || T <= 0 || H % H_kv != 0) return nullptr;
+  const char* name = attn_bwd_kernel_name(d, causal, which);
+  if (name == nullptr || check_device() != ATTN_OK) return nullptr;
+  if (which != 1 || dkdv_waves(B * H_kv, T) == kDkdvWaves) return name;
+  static const char* small[2][2] = {
+      {"attn_bwd_dkdv_bf16_d64_full_bk128_bq64_w4", "attn_bwd_dkdv_bf16_d64_causal_bk128_bq64_w4"},
+      {"attn_bwd_dkdv_bf16_d128_full_bk128_bq64_w4",
+       "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4"}};
+  return small[d == 128 ? 1 : 0][causal];
 }
 
 }  // extern "C"

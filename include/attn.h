@@ -172,6 +172,19 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v,
 const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
 
 /*
+ * Name of kernel `which` (as attn_bwd_kernel_name) that attn_bwd_gqa
+ * launches for these sizes on the current device, to inspect the instance
+ * actually selected ("FlashAttention -- avoid writing the giant
+ * intermediate", "Apply it at the right layer").  The dK/dV kernel takes
+ * 256-key workgroups of 8 waves, or 128-key workgroups of 4 waves
+ * ("attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4") when B * H_kv * ceil(T /
+ * 256) is below the device's CU count.  NULL for unsupported or
+ * non-positive sizes, or when the current device is not a gfx950.
+ */
+const char* attn_bwd_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t T, int64_t d,
+                                     int causal, int which);
+
+/*
  * Decode: Tq new queries per head over a key/value cache ("FlashAttention --
  * avoid writing the giant intermediate": short-input decode against the
  * stored key/value state, as opposed to long-input prefill).  The queries

@@ -1,0 +1,51 @@
+"""GPU parity of the dK/dV kernel's two instances.
+
+The backward's dK/dV kernel takes 256-key workgroups of 8 waves, or 128-key
+workgroups of 4 waves when the 256-key blocks of all key/value heads are
+fewer than the device's CUs.  Each case asserts the instance first, then
+checks sampled (or all) rows and keys of some heads against the float64
+oracle under the per-element bound of the backward tests.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from seeded_inputs import make_dout, make_qkv
+from test_gpu_bwd import U, check_head, gpu_backward, sampled
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def cus():
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+# (B, H, T, d): grids below and above the switch on a 256-CU device
+CASES = [(1, 8, 2048, 64), (1, 8, 2048, 128), (2, 3, 700, 128), (1, 1, 5000, 64),
+         (1, 32, 2048, 128), (2, 16, 2048, 64)]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("B,H,T,d", CASES)
+def test_dkdv_instances(B, H, T, d, causal):
+    import exact_attention_123_amd as ea
+    name = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 1)
+    small = B * H * ((T + 255) // 256) < cus()
+    want = "bk128_bq64_w4" if small else "bk256_bq64_w8"
+    assert name.endswith(want), name
+    say(f"[bwd instance] {name} B={B} H={H} T={T}")
+    scale = 1.0 / math.sqrt(d)
+    x = make_qkv(B, H, T, d, seed=8100 + T + d + H, qk_mult=2.0)
+    do = make_dout(B, H, T, d, seed=8200 + T + d)
+    res = gpu_backward(x, do, causal, scale)
+    for (b, h) in ((0, 0), (B - 1, H - 1)):
+        idx = sampled(T, 8300 + h) if T > 512 else None
+        check_head(x, do, b, h, res, causal, scale, rows=idx, keys=idx, ub=2 * U)
