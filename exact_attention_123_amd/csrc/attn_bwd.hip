@@ -198,15 +198,17 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
   ad.init(lane);
   TileDma<D, kTile, NW> dma;
   dma.init(wave, lane);
-  // Query tile `qt` of member `m` of the group (query head bhkv G + m).
+  // Query tile `qt` of member `m` of the group (query head bhkv G + m):
+  // part 0 its Q rows, part 1 its dO rows and row statistics, part 2 all.
   // Row statistics: one dword per lane of wave 0 (LSE) and wave 1 (-Delta),
   // lane L landing at 4 L; rows >= T read as zero.
-  auto stage = [&](char* tq, char* tg, float* tl, float* td, int m, int qt)
+  auto stage = [&](char* tq, char* tg, float* tl, float* td, int m, int qt, int part)
       __attribute__((always_inline)) {
     const size_t bhq = (size_t)bhkv * G + m;
     const size_t qhead = bhq * (size_t)T * D;
     const int row0 = qt * kTile;
-    dma.load(tq, Q + qhead, T, row0, wave);
+    if (part != 1) dma.load(tq, Q + qhead, T, row0, wave);
+    if (part == 0) return;
     dma.load(tg, dO + qhead, T, row0, wave);
     if (wave < 2) {
       const float* src = ws + (wave == 0 ? n : 0) + bhq * T + row0;
@@ -233,16 +235,22 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
   const int nqt = (T + kTile - 1) / kTile;
   const int per = nqt - qt0;  // > 0: k0 < T
   const int nit = G * per;
-  auto qt_of = [&](int it) __attribute__((always_inline)) {
-    return up ? qt0 + it % per : nqt - 1 - it % per;
+  // query tile at position r of a member's walk
+  auto qt_at = [&](int r) __attribute__((always_inline)) {
+    return up ? qt0 + r : nqt - 1 - r;
   };
-  // Query tile number `it` of the walk, staged in (tq, tg, tl, td).
-  auto tile = [&](const char* tq, const char* tg, const float* tl, const float* td, int it)
+  // Query tile qt, staged in (tq, tg, tl, td).  When st is set, the next
+  // tile's loads (member nm, tile nq_t, into (nq, ng, nl, nd)) are issued
+  // half before each sub-tile, rather than all at once when the waves leave
+  // the barrier.
+  auto tile = [&](const char* tq, const char* tg, const float* tl, const float* td, int qt,
+                  bool st, char* nq, char* ng, float* nl, float* nd, int nm, int nq_t)
       __attribute__((always_inline)) {
-    const int qt = qt_of(it);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i0 = qt * kTile + 32 * u;
+      if (st) stage(nq, ng, nl, nd, nm, nq_t, u);
+      __builtin_amdgcn_sched_barrier(0);
       // Nothing to add when every query of the sub-tile precedes every key
       // of the wave (causal) or lies past the end of the sequence (its Q
       // and dO rows read as zero).  Without a branch here the non-causal
@@ -274,13 +282,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
         }
       }
       if constexpr (!FOLD) S = f32x16_t{};
+      // S before dP, so that the exponentials of S overlap dP's MFMAs
 #pragma unroll
-      for (int s = 0; s < NDS; ++s) {
+      for (int s = 0; s < NDS; ++s)
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tq, 32 * u * RB + ad.row[s]),
                                                     lds_row(tk, kaddr[s]), S, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < NDS; ++s)
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tg, 32 * u * RB + ad.row[s]), vf[s],
                                                      dP, 0, 0, 0);
-      }
       if constexpr (FOLD) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) p[r] = exp2_hw(S[r] * c);
@@ -316,42 +326,53 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
           pb[a][e] = (__bf16)p[8 * a + e];
           db[a][e] = (__bf16)(p[8 * a + e] * dP[8 * a + e]);
         }
-      // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's 32 queries.
+      // dV^T += dO^T P, then dK^T += Q^T dS, over the sub-tile's 32 queries
+      // (dS is formed while the dV MFMAs run)
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int ro = (32 * u + 16 * a) * RB;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt)
           dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               lds_tr(tg, ro + ad.tr[0][dt], ro + ad.tr[1][dt]), pb[a], dv[dt], 0, 0, 0);
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int ro = (32 * u + 16 * a) * RB;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
           dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               lds_tr(tq, ro + ad.tr[0][dt], ro + ad.tr[1][dt]), db[a], dk[dt], 0, 0, 0);
-        }
       }
       // one sub-tile at a time: bounds the registers live at once
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  stage(sQ0, sG0, sL0, sD0, 0, qt_of(0));
+  stage(sQ0, sG0, sL0, sD0, 0, qt_at(0), 2);
   __syncthreads();
   // Two tiles per trip, alternating the stages: the loads of the next tile
   // run while this one is computed; the barrier after each tile waits for
   // them (and frees the stage just read).  No instruction is scheduled
   // across the tiles (sched_barrier), which keeps the register pressure of
-  // one tile.
+  // one tile.  (r, m): walk position and member of the tile computed, and
+  // (rn, mn) of the next one, advanced without divisions.
+  int r = 0, m = 0;
   for (int it = 0; it < nit; it += 2) {
-    if (it + 1 < nit) stage(sQ1, sG1, sL1, sD1, (it + 1) / per, qt_of(it + 1));
+    int rn = r + 1, mn = m;
+    if (rn == per) rn = 0, ++mn;
     ATTN_DEBUG_SYNC();
-    tile(sQ0, sG0, sL0, sD0, it);
+    tile(sQ0, sG0, sL0, sD0, qt_at(r), it + 1 < nit, sQ1, sG1, sL1, sD1, mn, qt_at(rn));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     if (it + 1 >= nit) break;
-    if (it + 2 < nit) stage(sQ0, sG0, sL0, sD0, (it + 2) / per, qt_of(it + 2));
+    r = rn, m = mn;
+    if (++rn == per) rn = 0, ++mn;
     ATTN_DEBUG_SYNC();
-    tile(sQ1, sG1, sL1, sD1, it + 1);
+    tile(sQ1, sG1, sL1, sD1, qt_at(r), it + 2 < nit, sQ0, sG0, sL0, sD0, mn, qt_at(rn));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
+    r = rn, m = mn;
   }
 
   store_rows<D>(dK + head, dk, scale, kw0 + j, T, h);
@@ -449,13 +470,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
       // every key of the sub-tile follows every query of the wave
       if (CAUSAL && kv0 > qw0 + 31) continue;
       f32x16_t S = f32x16_t{}, dP = dP0;
+      // S^T before dP^T, so that the exponentials overlap dP^T's MFMAs
 #pragma unroll
-      for (int s = 0; s < NDS; ++s) {
+      for (int s = 0; s < NDS; ++s)
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tk, 32 * u * RB + ad.row[s]), qf[s],
                                                     S, 0, 0, 0);
+#pragma unroll
+      for (int s = 0; s < NDS; ++s)
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(tv, 32 * u * RB + ad.row[s]), gf[s],
                                                      dP, 0, 0, 0);
-      }
       // Register 8 a + e of lane (j, h) holds key kv0 + 16 a + 8 h + e and
       // query qg.
       float p[16];
