@@ -18,9 +18,11 @@
 //             scale, or -LSE_i log2(e)) per query row, into the caller's
 //             workspace.
 //   2. dkdv : one workgroup of 8 waves per 256 keys of a head (32 per
-//             wave), K of those keys staged in LDS and V held in registers;
-//             it walks 64-query tiles of Q and dO (staged in LDS) and
-//             accumulates dV^T += dO^T P and dK^T += Q^T dS in registers.
+//             wave; 4 waves per 128 keys when the 256-key blocks of the
+//             problem are fewer than the device's CUs), K of those keys
+//             staged in LDS and V held in registers; it walks 64-query
+//             tiles of Q and dO (staged in LDS) and accumulates
+//             dV^T += dO^T P and dK^T += Q^T dS in registers.
 //   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
 //             registers; it walks 64-key tiles of K and V (staged in LDS)
 //             and accumulates dQ^T += K^T dS^T.
@@ -55,11 +57,9 @@ constexpr int kDkdvWavesSmall = 4;
 constexpr int kBK = 32 * kDkdvWaves;  // keys per dkdv workgroup (8 waves)
 constexpr int kBQ = 128;       // queries per dq workgroup
 constexpr int kTile = 64;      // rows of a staged Q/dO (dkdv) or K/V (dq) tile
-// Heads an XCD works on side by side in the dkdv and dq kernels (see their
-// workgroup order).  Measured on MI355X at B H = 32, T = 8192, causal (us
-// per call of the pass, one box): four (all of an XCD's heads) 1944, two
-// 1949, one at a time in dkdv 1968-1991; device-memory fetch of the dkdv
-// and dq kernels 1.56 GB per call with four, 0.87 GB with two.
+// Heads an XCD works on side by side in the dq kernel (see its workgroup
+// order): two read as fast as all four of an XCD's heads and fetch half the
+// device memory (0.40 against 0.81 GB per call at B H = 32, T = 8192).
 constexpr int kHeadsInFlight = 2;
 
 template <int D>
@@ -144,14 +144,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 31, h = lane >> 5;
   // Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each
-  // with its own L2.  When the heads split evenly over the XCDs in groups of
-  // kHeadsInFlight, XCD x takes its heads x, x + 8, ... in such groups, so
-  // that its CUs work on the key blocks of few heads at a time and share
-  // each Q and dO tile in L2 (with the walk below, the blocks of a head read
-  // the same tile at the same time); within a group, heavy-first (under a
-  // causal mask the first key blocks see the most query tiles) with the
-  // group's heads alternating.  Otherwise ids walk all heads within each
-  // key block.
+  // with its own L2.  When the key/value heads split evenly over the XCDs,
+  // XCD x takes its heads x, x + 8, ... one after the other, each head's key
+  // blocks heavy-first (under a causal mask the first key blocks see the
+  // most query tiles), and consecutive heads of an XCD walk their query
+  // tiles in opposite directions (`up`).  A CU that finishes the lightest
+  // block of one head then takes the next head's heaviest, so the CUs pair
+  // blocks kb and nkb - 1 - kb (equal work), and the blocks of a head that
+  // run side by side read the same Q and dO tile at the same time and share
+  // it in L2.  Otherwise ids walk all heads within each key block.
   const int id = blockIdx.x;
   int kb, bhkv;
   bool up = false;
