@@ -3,9 +3,10 @@
     python -m exact_attention_123_amd.build
 
 compiles ``csrc/attn_fwd.hip`` (forward), ``csrc/attn_bwd.hip`` (backward),
-``csrc/attn_decode.hip`` (decode over a key/value cache) and
-``csrc/attn_materialized.hip`` (the unfused three-kernel forward) and
-``csrc/mfma_probe.hip`` (the matrix-core throughput probe) with hipcc into
+``csrc/attn_decode.hip`` (decode over a key/value cache),
+``csrc/attn_materialized.hip`` (the unfused three-kernel forward),
+``csrc/mfma_probe.hip`` (the matrix-core throughput probe) and
+``csrc/device.hip`` (the host-side device checks they share) with hipcc into
 ``exact_attention_123_amd/libattn.so``, and the same sources with
 ``-DATTN_DEBUG_BARRIERS`` into ``libattn_debug_barriers.so`` (race check).
 The library exports the C ABI of ``include/attn.h``; the Python binding loads
@@ -22,7 +23,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", n)
         for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_materialized.hip",
-                  "mfma_probe.hip")]
+                  "mfma_probe.hip", "device.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 # The same library built with -DATTN_DEBUG_BARRIERS (extra workgroup barriers

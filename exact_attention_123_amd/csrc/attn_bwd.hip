@@ -38,15 +38,16 @@
 
 #include <cmath>
 #include <cstdint>
-#include <atomic>
-#include <cstring>
 
 #include "attn.h"
+#include "device.h"
 #include "tiles.h"
 
 namespace {
 
 using namespace attn_tiles;
+using attn_internal::check_device;
+using attn_internal::device_cus;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
@@ -544,14 +545,6 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-attn_status check_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
-}
-
 template <int D, bool FOLD, int NW>
 const void* dkdv_kernel(int causal) {
   return causal ? (const void*)attn_bwd_dkdv_kernel<D, true, FOLD, NW>
@@ -565,21 +558,6 @@ template <int D>
 const void* dkdv_kernel(int causal, bool fold, int nw) {
   return nw == kDkdvWavesSmall ? dkdv_kernel<D, kDkdvWavesSmall>(causal, fold)
                                : dkdv_kernel<D, kDkdvWaves>(causal, fold);
-}
-
-// Compute units of the current device (cached per device; 256 if unknown).
-std::atomic<int> g_cus[64];
-int device_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = g_cus[dev].load(std::memory_order_relaxed);
-  if (n <= 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      return 256;
-    g_cus[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
 }
 
 // Waves per dK/dV workgroup for these sizes: 4 when the 256-key blocks of

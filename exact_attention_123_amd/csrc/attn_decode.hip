@@ -38,10 +38,10 @@
 
 #include <cmath>
 #include <cstdint>
-#include <cstring>
 #include <mutex>
 
 #include "attn.h"
+#include "device.h"
 #include "fwd_cache.h"
 #include "rows.h"
 #include "tiles.h"
@@ -49,6 +49,7 @@
 namespace {
 
 using namespace attn_tiles;
+using attn_internal::check_device;
 using attn_rows::kBlk;
 using attn_rows::kMaxRows;
 using attn_rows::kThreads;
@@ -108,14 +109,6 @@ constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - 1;
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
-}
-
-attn_status check_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
 // Workgroups per (key/value head, split): one per 32 query rows.

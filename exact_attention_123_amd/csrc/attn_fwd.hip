@@ -39,13 +39,13 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
 
 #include "attn.h"
+#include "device.h"
 #include "fwd_cache.h"
 #include "rows.h"
 #include "tiles.h"
@@ -53,6 +53,8 @@
 namespace {
 
 using namespace attn_tiles;
+using attn_internal::check_device;
+using attn_internal::device_cus;
 
 // fp32 kernel: 4 waves, 128 query rows per workgroup (32 per wave).
 constexpr int kThreads = 256;
@@ -1011,26 +1013,6 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
   return ATTN_OK;
 }
 
-// Per-device cache of "is this a gfx950" (0 unknown, 1 yes, 2 no) and of
-// its compute-unit count.
-std::atomic<int> g_arch_ok[64];
-std::atomic<int> g_cus[64];
-
-attn_status check_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  if (dev < 0 || dev >= 64) return ATTN_ERR_DEVICE;
-  int s = g_arch_ok[dev].load(std::memory_order_relaxed);
-  if (s == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
-    s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
-    g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
-    g_arch_ok[dev].store(s, std::memory_order_relaxed);
-  }
-  return s == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
-}
-
 // Kernel of the bf16 forward for these sizes on the current device (after
 // check_device).  Problems whose grid of 256-row workgroups is smaller than
 // the device are bound by the latency of their longest query block, which
@@ -1050,12 +1032,7 @@ attn_status check_device() {
 enum class FwdPlan { kWaves8, kWaves4, kRows };
 
 FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d) {
-  int dev = 0;
-  int64_t cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    const int n = g_cus[dev].load(std::memory_order_relaxed);
-    if (n > 0) cus = n;
-  }
+  const int64_t cus = device_cus();
   if (B * H * ((T + 127) / 128) * (d / 64) <= cus) return FwdPlan::kRows;
   return B * H * ((T + 255) / 256) < cus ? FwdPlan::kWaves4 : FwdPlan::kWaves8;
 }
@@ -1064,12 +1041,7 @@ FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d) {
 // split over 4 waves) at d = 64 when its 128-row grid has fewer workgroups
 // than the device has CUs.
 bool f32_rows(int64_t B, int64_t H, int64_t T, int64_t d) {
-  int dev = 0;
-  int64_t cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    const int n = g_cus[dev].load(std::memory_order_relaxed);
-    if (n > 0) cus = n;
-  }
+  const int64_t cus = device_cus();
   return d == 64 && B * H * ((T + kBR - 1) / kBR) < cus;
 }
 
@@ -1196,14 +1168,7 @@ const char* w4_kernel_name(int64_t d, int causal) {
 namespace attn_internal {
 
 bool fwd_fills_device(int64_t B, int64_t H, int64_t Tq) {
-  check_device();  // caches the CU count (256 assumed without a device)
-  int dev = 0;
-  int64_t cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-    const int n = g_cus[dev].load(std::memory_order_relaxed);
-    if (n > 0) cus = n;
-  }
-  return B * H * ((Tq + 127) / 128) >= cus;
+  return B * H * ((Tq + 127) / 128) >= device_cus();
 }
 
 attn_status fwd_over_cache(const void* q, const void* k, const void* v, void* o, float* lse,

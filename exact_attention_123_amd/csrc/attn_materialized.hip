@@ -26,11 +26,13 @@
 #include <cstring>
 
 #include "attn.h"
+#include "device.h"
 #include "tiles.h"
 
 namespace {
 
 using namespace attn_tiles;
+using attn_internal::check_device;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -246,14 +248,6 @@ __global__ __launch_bounds__(kThreads) void attn_mat_pv_kernel(
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
-}
-
-attn_status check_device() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
 template <int D>

@@ -1,6 +1,6 @@
 """AddressSanitizer build of the library's host code (CPU, no GPU needed).
 
-The four HIP sources are compiled with the host side instrumented (the GPU
+The HIP sources are compiled with the host side instrumented (the GPU
 code is not), linked with a small driver (tests/asan/abi_driver.cpp) that
 drives every entry point of include/attn.h through argument validation,
 empty problems, size queries, kernel names and status strings, and run.
@@ -23,7 +23,8 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 def test_host_code_under_address_sanitizer(tmp_path):
     exe = str(tmp_path / "abi_asan")
     srcs = [os.path.join(CSRC, f) for f in
-            ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_materialized.hip")]
+            ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_materialized.hip",
+             "device.hip")]
     cmd = [HIPCC, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-fsanitize=address", "-fno-gpu-sanitize", "-fno-omit-frame-pointer",
