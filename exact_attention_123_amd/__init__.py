@@ -307,8 +307,8 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
     and ``lse`` are what :func:`forward` returned for the same q, k, v,
     causal and scale; ``dout`` is the gradient of o.  Returns (dq, dk, dv)
     shaped like q, k, v.  ``ws`` is an optional float32 workspace of 2*B*H*T
-    elements (allocated when None); after the call it holds Delta and
-    lse*log2(e).
+    elements (allocated when None); after the call it holds -Delta, then
+    -lse/scale (-lse*log2(e) when |scale| < 2^-32), each [B, H, T].
     """
     import torch
 
