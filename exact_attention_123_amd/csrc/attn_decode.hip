@@ -75,26 +75,65 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
 }
 
 // Merge of the splits: one wave per query row, D / 64 columns per lane.
+// The row's log-sum-exp over the splits, lse = ln sum_s exp(lse_s), comes
+// from wave reductions over lanes that each hold splits lane, lane + 64, ...;
+// then O = sum_s exp(lse_s - lse) O_s, with kUnroll splits' partial rows
+// loaded at a time and each split's weight read from the lane that holds
+// it.  (A loop over the splits one load at a time is a chain of 3 nsplit
+// dependent memory round trips: 20 us for 32 splits.)
+constexpr int kCombineUnroll = 16;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, __bf16* __restrict__ O,
     float* __restrict__ LSE, int NR, int nsplit) {
   constexpr int CPL = D / 64;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // one per wave
   const int lane = threadIdx.x & 63;
-  if (row >= NR) return;
+  if (row >= NR) return;  // the whole wave
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_lse[(size_t)s * NR + row]);
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_lse[(size_t)s * NR + row]);
+  M = wave_max(M);
   float L = 0.0f;
-  for (int s = 0; s < nsplit; ++s)
+  for (int s = lane; s < nsplit; s += 64)
     L += exp2_hw((part_lse[(size_t)s * NR + row] - M) * kLog2e);
-  const float lse = M + log2_hw(L) * kLn2;
+  const float lse = M + log2_hw(wave_sum(L)) * kLn2;
   float o[CPL] = {};
-  for (int s = 0; s < nsplit; ++s) {
-    const float wgt = exp2_hw((part_lse[(size_t)s * NR + row] - lse) * kLog2e);
-    const float* src = part_o + ((size_t)s * NR + row) * D + lane * CPL;
+  const float* src = part_o + (size_t)row * D + lane * CPL;
+  const size_t split_stride = (size_t)NR * D;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    // weight of split s0 + lane
+    const int sl = s0 + lane;
+    const float w = sl < nsplit ? exp2_hw((part_lse[(size_t)sl * NR + row] - lse) * kLog2e) : 0.0f;
+    const int n = min(64, nsplit - s0);
+    for (int i = 0; i < n; i += kCombineUnroll) {
+      float v[kCombineUnroll][CPL];
 #pragma unroll
-    for (int u = 0; u < CPL; ++u) o[u] = fmaf(wgt, src[u], o[u]);
+      for (int k = 0; k < kCombineUnroll; ++k)
+#pragma unroll
+        for (int u = 0; u < CPL; ++u)
+          v[k][u] = i + k < n ? src[(size_t)(s0 + i + k) * split_stride + u] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCombineUnroll; ++k) {
+        // lanes i + k < 64 always (i < n <= 64, and the weight of a lane
+        // past the last split is 0)
+        const float wk = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), (i + k) & 63));
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) o[u] = fmaf(wk, v[k][u], o[u]);
+      }
+    }
   }
 #pragma unroll
   for (int u = 0; u < CPL; ++u) O[(size_t)row * D + lane * CPL + u] = (__bf16)o[u];

@@ -135,6 +135,22 @@ def test_decode_many_splits():
         check(x, O, L, causal, scale, Tk)
 
 
+@pytest.mark.parametrize("Tk,nsplit,d", [(262144, 64, 128), (266240, 65, 64),
+                                          (326680, 80, 128)])
+def test_decode_splits_past_one_wave(Tk, nsplit, d):
+    """More key splits than a wave has lanes: the merge of the splits takes
+    their log-sum-exps 64 at a time (64, 65 and 80 splits; ragged length)."""
+    import exact_attention_123_amd as ea
+    B, H, Hkv, Tq = 1, 4, 1, 2
+    assert ea.decode_splits(B, H, Hkv, Tq, Tk) == nsplit
+    say(f"[decode {nsplit} splits] B={B} H={H} Hkv={Hkv} Tq={Tq} Tk={Tk} d={d}")
+    x = make_decode(B, H, Hkv, Tq, Tk, d, seed=9250 + nsplit, qk_mult=4.0)
+    scale = 1.0 / math.sqrt(d)
+    for causal in (True, False):
+        O, L = run_decode(x, causal, scale, Tk)
+        check(x, O, L, causal, scale, Tk)
+
+
 def test_decode_matches_square_forward_rows():
     """The GPU decode of the last Tq positions against the GPU forward over
     the full square problem (its last Tq rows): the two paths agree within
