@@ -57,8 +57,10 @@ using attn_rows::kWaves;
 
 // Key split: about kTargetGroups workgroups (one round at two per CU), each
 // split at least kMinSplitKeys long: short splits cost a prologue, an LDS
-// merge and partial results each (measured: 32 splits of 4096 keys read a
-// 131072-key cache at 4.7 TB/s, 128 splits of 1024 keys at 3.3 TB/s).
+// merge and partial results each (measured on MI355X, us per call of one
+// 131072-key sequence with 32 query / 8 key-value heads: 32 splits of 4096
+// keys 97.9, 64 of 2048 100.1, 128 of 1024 109.0; a target of 256 instead
+// of 512 costs 3% on 16 sequences of 32768 keys).
 constexpr int kMinSplitKeys = 4096;
 constexpr int kTargetGroups = 512;
 
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
 // Merge of the splits: one wave per query row, D / 64 columns per lane.
 // The row's log-sum-exp over the splits, lse = ln sum_s exp(lse_s), comes
 // from wave reductions over lanes that each hold splits lane, lane + 64, ...;
-// then O = sum_s exp(lse_s - lse) O_s, with kUnroll splits' partial rows
+// then O = sum_s exp(lse_s - lse) O_s, with kCombineUnroll splits' partial rows
 // loaded at a time and each split's weight read from the lane that holds
 // it.  (A loop over the splits one load at a time is a chain of 3 nsplit
 // dependent memory round trips: 20 us for 32 splits.)
