@@ -1056,8 +1056,10 @@ constexpr bool kRowsKLds = D == 64 || NW == 4;
 // Square forward on the row-chunk kernel: Tq = Tk = T, one key split (the
 // chunk's keys are cut only between its NW waves), O and LSE written
 // directly.
+// Two workgroups per CU at d = 64; at d = 128 the K and V stages of one
+// 4-wave workgroup take 128 KiB of LDS, so one.
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void attn_fwd_rows_kernel(
+__global__ __launch_bounds__(64 * NW, NW == 4 && D == 64 ? 2 : 1) void attn_fwd_rows_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int G, int NR, int nwg, float c) {
   attn_rows::row_chunk_attention<D, CAUSAL, NW, kRowsKLds<D, NW>>(
