@@ -80,10 +80,18 @@ def code_sha(text: str) -> str:
 
 
 def source_sha(pass_: str = "fwd") -> str:
+    """code_sha of the pass's sources, each followed by the compiler options
+    the library build gives that file alone (build.FILE_FLAGS), so that a
+    change of those options also invalidates the pass's summaries."""
+    from .build import FILE_FLAGS
+
     text = ""
     for path in SOURCES[pass_]:
         with open(path) as f:
             text += f.read() + "\n"
+        flags = FILE_FLAGS.get(os.path.basename(path))
+        if flags:
+            text += "compiler options: " + " ".join(flags) + "\n"
     return code_sha(text)
 
 
