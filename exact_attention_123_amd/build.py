@@ -32,14 +32,20 @@ LIB = os.path.join(PKG, "libattn.so")
 DEBUG_LIB = os.path.join(PKG, "libattn_debug_barriers.so")
 
 ARCH = "gfx950"
-# Compiler options of single sources, on top of HIPCC_FLAGS.  The forward
-# kernels are scheduled with LLVM's memory-clause strategy: 525.0 against
-# 527.6 us per call at B H = 32, T = 8192, d = 128, causal (A/B in one
-# process on MI355X, twice; bit-identical outputs).  The same strategy makes
-# the backward's dK/dV kernel spill (1899 against 1681 us), and the ILP
-# strategy is slower for both.
+# Compiler options of single sources, on top of HIPCC_FLAGS (A/B in one
+# process on MI355X at B H = 32, T = 8192, d = 128, causal; bit-identical
+# outputs):
+#  - the forward kernels are scheduled with LLVM's memory-clause strategy:
+#    525.0 against 527.6 us per call (twice); the same strategy makes the
+#    backward's dK/dV kernel spill (1899 against 1681 us), and the ILP
+#    strategy is slower for both;
+#  - the backward's scheduler uses the AMDGPU register-pressure trackers:
+#    1649.5 against 1665.6 and 1686.4 against 1699.4 us per call (two
+#    boxes); for the forward they change nothing measurable, nor does the
+#    occupancy / latency bias of the scheduler for either.
 FILE_FLAGS = {
     "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"],
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers"],
 }
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
