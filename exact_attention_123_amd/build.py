@@ -7,8 +7,10 @@ compiles ``csrc/attn_fwd.hip`` (forward), ``csrc/attn_bwd.hip`` (backward),
 ``csrc/attn_materialized.hip`` (the unfused three-kernel forward),
 ``csrc/mfma_probe.hip`` (the matrix-core throughput probe) and
 ``csrc/device.hip`` (the host-side device checks they share) with hipcc into
-``exact_attention_123_amd/libattn.so``, and the same sources with
-``-DATTN_DEBUG_BARRIERS`` into ``libattn_debug_barriers.so`` (race check).
+``exact_attention_123_amd/libattn.so``, the same sources with
+``-DATTN_DEBUG_BARRIERS`` into ``libattn_debug_barriers.so`` (race check),
+and the plain C caller of the ABI used by a GPU test
+(``tests/c_abi/libattn_c_caller.so``).
 The library exports the C ABI of ``include/attn.h``; the Python binding loads
 it with ctypes.
 """
@@ -111,6 +113,30 @@ def build(verbose: bool = False, out: str = LIB, debug_barriers: bool = False) -
     return out
 
 
+# A plain C99 caller of the C ABI (tests/c_abi/c_caller.c), built next to its
+# source and linked against libattn.so; a GPU test loads it.
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi", "c_caller.c")
+C_CALLER_LIB = os.path.join(ROOT, "tests", "c_abi", "libattn_c_caller.so")
+
+
+def build_c_caller(verbose: bool = False) -> str:
+    """Compile the C caller with the host C compiler (after build()); returns
+    its path.  Raises on compiler errors."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler (gcc) found")
+    tmp = C_CALLER_LIB + ".tmp"
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-fPIC", "-shared",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-I", INCLUDE,
+           C_CALLER_SRC, "-o", tmp, "-L", PKG, "-lattn", "-L", os.path.join(rocm, "lib"),
+           "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../../exact_attention_123_amd"]
+    _finish(_run(cmd, verbose), verbose)
+    os.replace(tmp, C_CALLER_LIB)
+    return C_CALLER_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
     print(build(verbose="-v" in sys.argv, out=DEBUG_LIB, debug_barriers=True))
+    print(build_c_caller(verbose="-v" in sys.argv))

@@ -343,3 +343,18 @@ def test_probe_validation_and_flop_count():
     assert f(0, 3, 10) == 3 * 4 * 10 * 16 * 2 * 32 * 32 * 16
     assert f(1, 3, 10) == 3 * 4 * 10 * 32 * 2 * 16 * 16 * 32
     assert f(5, 3, 10) == 0.0
+
+
+def test_c_caller_built():
+    """The plain C caller of the ABI (tests/c_abi/c_caller.c) is built by the
+    library build and runs its checks or, without a GPU, reports the HIP call
+    that failed (no crash)."""
+    from exact_attention_123_amd.build import C_CALLER_LIB
+    assert os.path.exists(C_CALLER_LIB), "build it with python -m exact_attention_123_amd.build"
+    lib = ctypes.CDLL(C_CALLER_LIB)
+    lib.attn_c_caller_check.restype = ctypes.c_int
+    lib.attn_c_caller_check.argtypes = [ctypes.c_char_p, ctypes.c_int]
+    msg = ctypes.create_string_buffer(256)
+    rc = lib.attn_c_caller_check(msg, len(msg))
+    text = msg.value.decode()
+    assert (rc == 0 and "passed" in text) or (rc != 0 and "failed" in text), (rc, text)
