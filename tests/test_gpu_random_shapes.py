@@ -107,3 +107,51 @@ def test_random_problem(case):
             el = max(el, max_err(L[b, h][r], ref["LSE"]))
         to, tl = TOL[dt]
     assert eo <= to and el <= tl, (eo, el)
+
+
+LARGE_CASES = 12
+
+
+@pytest.mark.parametrize("case", range(LARGE_CASES))
+def test_random_large_forward(case):
+    """Seeded random bf16 forward problems on grids that fill the GPU (the
+    4-wave and 8-wave instances, which the draws above reach only twice):
+    B in {1, 2, 4}, 4 to 32 key/value heads with G = 1, 2 or 4 query heads
+    each, T from 512 to 8192 (at most 2^27 elements per tensor), both masks,
+    the scales 1, 0.5, -0.7 and 0 (over sqrt(d)) in turn, Q and K times 1, 2
+    or 4; sampled rows of three heads against the oracle at the bf16
+    tolerances."""
+    import torch
+
+    import exact_attention_123_amd as ea
+    rng = np.random.Generator(np.random.PCG64(93000 + case))
+    B = int(rng.choice([1, 2, 4]))
+    Hkv = int(rng.choice([4, 8, 16, 32]))
+    G = int(rng.choice([1, 2, 4]))
+    H = Hkv * G
+    d = int(rng.choice([64, 128]))
+    T = int(np.exp(rng.uniform(np.log(512), np.log(8192))))
+    T = min(T, (1 << 27) // (B * H * d))
+    causal = bool(rng.integers(2))
+    scale = (1.0, 0.5, -0.7, 0.0)[case % 4] / math.sqrt(d)
+    mult = float(rng.choice([1.0, 2.0, 4.0]))
+    name = ea.fwd_kernel_name_for(B, H, T, d, causal)
+    say(f"case {case}: fwd B={B} H={H} Hkv={Hkv} T={T} d={d} causal={causal} "
+        f"scale={scale:.4f} qk x{mult}: {name}")
+    x = make_qkv(B, H, T, d, seed=94000 + case, qk_mult=mult, H_kv=Hkv)
+    q, k, v = (to_device(a, "bf16") for a in (x.q, x.k, x.v))
+    o, lse = ea.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    eo = el = 0.0
+    for i in rng.choice(len(heads), size=3, replace=False):
+        b, h = heads[i]
+        r = sampled_rows(rng, T, 24)
+        got_o = to64(o[b, h][torch.from_numpy(r).cuda()], "bf16")
+        got_l = lse[b, h][torch.from_numpy(r).cuda()].cpu().numpy().astype(np.float64)
+        ref = oracle.attention_head(x.q64(b, h), x.k64(b, h // G), x.v64(b, h // G),
+                                    causal=causal, scale=scale, rows=r)
+        eo = max(eo, max_err(got_o, ref["O"]))
+        el = max(el, max_err(got_l, ref["LSE"]))
+    to, tl = TOL["bf16"]
+    assert eo <= to and el <= tl, (eo, el)
