@@ -8,7 +8,10 @@ cases put heads past the 2^31- and 2^32-byte marks of their tensors, where a
     [B, H, T, d] tensor 4.36 GB; head 1024 starts at byte 2^31 and head 2048
     at byte 2^32), and the grouped forward with 13 key/value heads;
   - decode over a cache of 16 sequences x 8 key/value heads x 140000 keys
-    (4.59 GB per cache tensor; ragged length).
+    (4.59 GB per cache tensor; ragged length);
+  - decode of one head at the longest cache the library accepts
+    (8388543 keys at d = 128), against a closed form, and the shape error
+    one key beyond it.
 
 Inputs are seeded draws made on the device (torch's generator), so the
 large tensors never cross to the host; the heads that are checked (the
@@ -166,4 +169,37 @@ def test_decode_over_4gib_cache():
             f"O err {eo:.3e} LSE err {el:.3e}")
         assert eo <= TOL_O and el <= TOL_LSE
     del q, kc, vc, o, lse
+    free()
+
+
+def test_decode_at_the_maximum_cache_length():
+    """One head at the longest cache attn_decode accepts at d = 128 (a head of
+    2^31 - 1 bytes holds Tk_cap + 64 rows): with Q = 0 every score is 0, so
+    the single new query's output is the mean of all V rows and its LSE is
+    ln(Tk), checked on the host from V read back in chunks; one key more is
+    rejected as a shape error."""
+    import torch
+
+    import exact_attention_123_amd as ea
+    d = 128
+    Tk = (2 ** 31 - 1) // (d * 2) - 64
+    say(f"[max decode] Tk={Tk} d={d}: {Tk * d * 2 / 1e9:.2f} GB per cache tensor")
+    q = torch.zeros((1, 1, 1, d), dtype=torch.bfloat16, device="cuda")
+    kc, vc = draw((1, 1, Tk, d), 111), draw((1, 1, Tk, d), 112)
+    o, lse = ea.decode(q, kc, vc, causal=True, scale=1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    mean = np.zeros(d)
+    step = 1 << 20
+    for t0 in range(0, Tk, step):
+        mean += vc[0, 0, t0:t0 + step].double().sum(0).cpu().numpy()
+    mean /= Tk
+    eo = float(np.abs(o[0, 0, 0].double().cpu().numpy() - mean).max())
+    el = abs(float(lse[0, 0, 0]) - math.log(Tk))
+    say(f"    O err {eo:.3e} LSE err {el:.3e} (splits {ea.decode_splits(1, 1, 1, 1, Tk)})")
+    assert eo <= TOL_O and el <= TOL_LSE
+    big = torch.empty((1, 1, Tk + 1, d), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ea.AttnError) as err:
+        ea.decode(q, big, big.clone(), causal=True)
+    assert err.value.code == 2  # ATTN_ERR_SHAPE
+    del q, kc, vc, o, lse, big
     free()
