@@ -29,9 +29,12 @@ comparison.
 Timing: W untimed warm-up steps, then untimed steps until --settle-ms (default
 2 s) of wall time has passed since the warm-up began (the shader clock of a
 cold GPU needs a few hundred launches to reach its loaded steady state), then
-K steps between HIP events on the launch stream.  The record carries the
-settle phase's length, the first and last five launch durations, and the
-shader and memory clocks, socket power and power-limit residency sampled
+K steps between two HIP events on the launch stream (none between the steps:
+the value and the roofline both come from this region's average step).  After
+the region, K more steps, each between its own pair of events, give the
+spread of launch durations.  The record carries the settle phase's length,
+that spread (minimum, maximum, median, the first and last five launches), and
+the shader and memory clocks, socket power and power-limit residency sampled
 (amdsmi, host-side) over the settle phase's last 500 ms and over the timed
 region.
 
@@ -248,11 +251,15 @@ class GpuMetricsSampler:
 def time_steps(step, stream, steps: int, warmup: int, settle_ms: float = 0.0, sampler=None):
     """W untimed steps, then (untimed) more steps until `settle_ms` of wall
     time has passed since the warm-up began, so that the clocks reach their
-    loaded steady state; then K steps between HIP events on the launch
-    stream.  Returns (per-step ms list, region ms, wall s, info) with info
-    holding the settle phase's length and, when a sampler runs, the clock
-    and power summary of the settle phase's last 500 ms and of the timed
-    region."""
+    loaded steady state; then the timed region: K steps between one pair of
+    HIP events on the launch stream, none between the steps (an event pair
+    per step adds several microseconds of device time to each step, half
+    again on a 15 us launch); then, after the region, K more steps each
+    between its own pair of events, for the spread of launch durations.
+    Returns (per-step ms list of that spread pass, region ms, wall s of the
+    region, info) with info holding the settle phase's length and, when a
+    sampler runs, the clock and power summary of the settle phase's last
+    500 ms and of the timed region."""
     import torch
 
     t_warm = time.perf_counter()
@@ -266,28 +273,45 @@ def time_steps(step, stream, steps: int, warmup: int, settle_ms: float = 0.0, sa
         settle_steps += 8
         torch.cuda.synchronize()
     t_settled = time.perf_counter()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    r0.record(stream)
+    for _ in range(steps):
+        step()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
     per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     info = {"settle_ms": round((t_settled - t_warm) * 1e3, 1), "settle_steps": settle_steps,
             "warmup_steps": warmup}
     if sampler is not None:
-        time.sleep(3 * sampler.period)  # one more sample after the region ends
+        time.sleep(3 * sampler.period)  # one more sample after the spread pass
         sampler.stop()
         info["clocks_settle_last_500ms"] = sampler.window(t_settled - 0.5, t_settled)
-        # the sample just after the region closes it (the accumulators are
+        # the first sample after the region closes it (the accumulators are
         # differenced between the first and last samples of the window)
-        info["clocks_timed_region"] = sampler.window(t0, t1 + 3 * sampler.period)
-    return per, starts[0].elapsed_time(ends[-1]), wall, info
+        info["clocks_timed_region"] = sampler.window(t0, t1 + sampler.period)
+    return per, r0.elapsed_time(r1), wall, info
+
+
+def timing_record(region_ms: float, steps: int, wall: float, per, tinfo) -> dict:
+    """The record's timing block: the timed region's average step, and the
+    spread pass's average, minimum, maximum, median and first and last five
+    launch durations (ms)."""
+    return {"avg_launch_ms": round(region_ms / steps, 4), "wall_s": round(wall, 3),
+            "spread_pass": {"avg_launch_ms": round(sum(per) / len(per), 4),
+                            "min_launch_ms": round(min(per), 4),
+                            "max_launch_ms": round(max(per), 4), **launch_spread(per)},
+            **tinfo}
 
 
 def mfma_ceiling(dev, sampler=None, shape: int = 0):
@@ -328,8 +352,8 @@ def mfma_ceiling(dev, sampler=None, shape: int = 0):
 
 
 def launch_spread(per):
-    """Median and the first and last five launch durations (ms) of the
-    timed region."""
+    """Median and the first and last five launch durations (ms) of a pass
+    timed launch by launch."""
     srt = sorted(per)
     mid = len(srt) // 2
     median = srt[mid] if len(srt) % 2 else 0.5 * (srt[mid - 1] + srt[mid])
@@ -423,12 +447,11 @@ def run_decode(args) -> int:
                                              args.settle_ms, sampler)
     copy_calibration(args.copy_calibration_mib, dev)
     ms_per_step = region_ms / args.steps
-    avg_ms = sum(per) / len(per)
     nbytes = (2 * B * Hkv * Tk * d * 2      # valid K and V cache rows, read once
               + 2 * B * H * Tq * d * 2      # Q read, O written
               + B * H * Tq * 4)             # LSE written
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    achieved = value  # one launch per step, averaged over the timed region
     kname = f"attn_decode_bf16_d{d}_{'causal' if causal else 'full'}_w4_blk32"
     traffic = measured_traffic(kname, name, "decode")
     res = {
@@ -451,9 +474,7 @@ def run_decode(args) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
-        "timing": {"avg_launch_ms": round(avg_ms, 4), "min_launch_ms": round(min(per), 4),
-                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3),
-                   **launch_spread(per), **tinfo},
+        "timing": timing_record(region_ms, args.steps, wall, per, tinfo),
         "parity": parity,
     }
     if not args.no_cpu_baseline:
@@ -546,12 +567,12 @@ def run_mat(args) -> int:
     per, region_ms, wall, tinfo = time_steps(step, stream, steps, warm)
     o2 = torch.empty_like(q)
     l2 = torch.empty_like(lse)
-    fper, _, _, _ = time_steps(lambda: ea.forward(q, k, v, causal=causal, scale=scale, out=o2,
-                                                  lse=l2), stream, steps, warm)
+    _, fused_region_ms, _, _ = time_steps(lambda: ea.forward(q, k, v, causal=causal, scale=scale,
+                                                             out=o2, lse=l2), stream, steps, warm)
     copy_calibration(args.copy_calibration_mib, dev)
     ms_per_step = region_ms / steps
-    avg_ms = sum(per) / len(per)
-    fused_ms = sum(fper) / len(fper)
+    avg_ms = ms_per_step
+    fused_ms = fused_region_ms / steps
     fl = ea.flops(B, H, T, d, causal)
     nbytes = mat_bytes(B, H, T, d, causal)
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
@@ -578,9 +599,7 @@ def run_mat(args) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(kname, name, "mat")},
-        "timing": {"avg_launch_ms": round(avg_ms, 4), "min_launch_ms": round(min(per), 4),
-                   "max_launch_ms": round(max(per), 4), "wall_s": round(wall, 3),
-                   **launch_spread(per), **tinfo},
+        "timing": timing_record(region_ms, steps, wall, per, tinfo),
         "compare": {"fused_fwd_avg_ms": round(fused_ms, 4),
                     "materialised_over_fused": round(avg_ms / fused_ms, 2)},
         "parity": parity,
@@ -744,7 +763,7 @@ def main() -> int:
     per_launch_ms, region_ms, wall, tinfo = time_steps(step, stream, args.steps, args.warmup,
                                                        args.settle_ms, sampler)
     ms_per_step = region_ms / args.steps
-    avg_launch_ms = sum(per_launch_ms) / len(per_launch_ms)
+    avg_launch_ms = ms_per_step  # one launch (one call) per step
     copy_calibration(args.copy_calibration_mib, dev)
 
     ceiling = None
@@ -797,10 +816,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic},
-        "timing": {"avg_launch_ms": round(avg_launch_ms, 4),
-                   "min_launch_ms": round(min(per_launch_ms), 4),
-                   "max_launch_ms": round(max(per_launch_ms), 4),
-                   "wall_s": round(wall, 3), **launch_spread(per_launch_ms), **tinfo},
+        "timing": timing_record(region_ms, args.steps, wall, per_launch_ms, tinfo),
         "parity": parity,
     }
     if ceiling is not None:

@@ -239,6 +239,33 @@ def _check_same_device(ts, names: str) -> None:
         raise ValueError(f"{names} must all be on the same device")
 
 
+_raw_stream = None
+_get_device = None
+
+
+def _launch(dev, stream, entry, *args) -> int:
+    """Calls the raw entry point ``entry(*args, stream_handle)`` with ``dev``
+    as the current device (the library launches on the current device) and
+    the handle of ``stream``, else of dev's current stream.  The handle and
+    the current device are read through torch's direct accessors where it
+    has them (a few hundred ns, against microseconds for a Stream object and
+    a device guard), so that the host keeps ahead of kernels of tens of
+    microseconds."""
+    global _raw_stream, _get_device
+    import torch
+
+    if _raw_stream is None:
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream",
+                              lambda i: torch.cuda.current_stream(i).cuda_stream)
+        _get_device = getattr(torch._C, "_cuda_getDevice", torch.cuda.current_device)
+    idx = dev.index
+    s = stream.cuda_stream if stream is not None else _raw_stream(idx)
+    if _get_device() == idx:
+        return entry(*args, s)
+    with torch.cuda.device(dev):
+        return entry(*args, s)
+
+
 def flops(B: int, H: int, T: int, d: int, causal: bool) -> float:
     """Counted FLOPs of one forward: the two T x T x d contractions,
     4*T*T*d per head, halved under a causal mask."""
@@ -286,14 +313,12 @@ def forward(q, k, v, causal: bool = True, scale: float | None = None, out=None, 
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     _check_buffer(out, "out", q.shape, q.dtype, q.device)
     _check_buffer(lse, "lse", (B, H, T), torch.float32, q.device)
-    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    with torch.cuda.device(q.device):
-        if q.dtype == torch.float32:
-            st = attn_fwd_f32(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              lse.data_ptr(), B, H, T, d, causal, scale, s)
-        else:
-            st = attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                              lse.data_ptr(), B, H, Hkv, T, d, causal, scale, s)
+    if q.dtype == torch.float32:
+        st = _launch(q.device, stream, attn_fwd_f32, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     out.data_ptr(), lse.data_ptr(), B, H, T, d, causal, scale)
+    else:
+        st = _launch(q.device, stream, attn_fwd_gqa, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     out.data_ptr(), lse.data_ptr(), B, H, Hkv, T, d, causal, scale)
     if st != 0:
         raise AttnError(st, status_string(st))
     return out, lse
@@ -340,11 +365,9 @@ def backward(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = N
         raise ValueError("ws must be a contiguous float32 tensor of 2*B*H*T elements")
     if ws.device != q.device:
         raise ValueError(f"ws must be on {q.device}")
-    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    with torch.cuda.device(q.device):
-        st = attn_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                          dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                          dv.data_ptr(), ws.data_ptr(), B, H, Hkv, T, d, causal, scale, s)
+    st = _launch(q.device, stream, attn_bwd_gqa, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                 o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                 dv.data_ptr(), ws.data_ptr(), B, H, Hkv, T, d, causal, scale)
     if st != 0:
         raise AttnError(st, status_string(st))
     return dq, dk, dv
@@ -385,11 +408,9 @@ def decode(q, k_cache, v_cache, Tk: int | None = None, causal: bool = True,
         raise ValueError(f"ws must be a contiguous tensor on {q.device}")
     ws_ptr = ws.data_ptr() if ws is not None else 0
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    with torch.cuda.device(q.device):
-        st = attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
-                         lse.data_ptr(), ws_ptr, ws_bytes, B, H, Hkv, Tq, Tk, Tcap, d, causal,
-                         scale, s)
+    st = _launch(q.device, stream, attn_decode, q.data_ptr(), k_cache.data_ptr(),
+                 v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes, B, H, Hkv,
+                 Tq, Tk, Tcap, d, causal, scale)
     if st != 0:
         raise AttnError(st, status_string(st))
     return out, lse
@@ -423,11 +444,9 @@ def forward_materialized(q, k, v, causal: bool = True, scale: float | None = Non
     _check_buffer(lse, "lse", (B, H, T), torch.float32, q.device)
     _check_buffer(s_buf, "s_buf", (B, H, T, T), torch.float32, q.device)
     _check_buffer(p_buf, "p_buf", (B, H, T, T), torch.bfloat16, q.device)
-    s = (stream or torch.cuda.current_stream(q.device)).cuda_stream
-    with torch.cuda.device(q.device):
-        st = attn_fwd_materialized(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                   lse.data_ptr(), s_buf.data_ptr(), p_buf.data_ptr(), B, H, T,
-                                   d, causal, scale, s)
+    st = _launch(q.device, stream, attn_fwd_materialized, q.data_ptr(), k.data_ptr(),
+                 v.data_ptr(), out.data_ptr(), lse.data_ptr(), s_buf.data_ptr(),
+                 p_buf.data_ptr(), B, H, T, d, causal, scale)
     if st != 0:
         raise AttnError(st, status_string(st))
     return out, lse

@@ -48,6 +48,18 @@ def test_launch_spread_and_blas_info():
     assert isinstance(info, list)
 
 
+def test_timing_record_takes_the_region_average():
+    """The record's average step is the timed region's (no events inside
+    it); the per-launch pass after it gives only the spread."""
+    per = [2.0, 4.0, 3.0]
+    r = bench.timing_record(9.3, 3, 0.01, per, {"settle_ms": 2000.0})
+    assert r["avg_launch_ms"] == 3.1
+    assert r["spread_pass"]["avg_launch_ms"] == 3.0
+    assert r["spread_pass"]["min_launch_ms"] == 2.0 and r["spread_pass"]["max_launch_ms"] == 4.0
+    assert r["spread_pass"]["median_launch_ms"] == 3.0
+    assert r["settle_ms"] == 2000.0 and r["wall_s"] == 0.01
+
+
 def test_multi_gpu_request_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)

@@ -211,3 +211,37 @@ def test_empty_and_stream_and_no_allocation():
                                     scale=1 / math.sqrt(128))
         eo = max(eo, max_err(O[0, h], ref["O"]))
     assert eo <= TOL["bf16"][0]
+
+
+def test_launches_follow_the_stream():
+    """The binding launches on the stream it is given (stream=) or, without
+    one, on the current stream: after work queued there before it.  Q is
+    copied in on a side stream behind about 20 ms of matrix products; a launch
+    on any other stream would run while Q is still zero (O would be the mean
+    of the visible V rows)."""
+    import torch
+    x = make_qkv(1, 4, 1024, 128, dtype="bf16", seed=86)
+    qd, kd, vd = (to_device(a, "bf16") for a in (x.q, x.k, x.v))
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    s = torch.cuda.Stream()
+    refs = [oracle.attention_head(x.q64(0, h), x.k64(0, h), x.v64(0, h), causal=True,
+                                  scale=1 / math.sqrt(128))["O"] for h in range(4)]
+    for how in ("stream=", "current stream"):
+        say(f"[stream] {how}")
+        q2 = torch.zeros_like(qd)
+        out = torch.empty_like(qd)
+        lse = torch.empty((1, 4, 1024), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            for _ in range(16):
+                b = a @ a
+            q2.copy_(qd)
+            if how == "current stream":
+                ea.forward(q2, kd, vd, causal=True, out=out, lse=lse)
+        if how == "stream=":
+            ea.forward(q2, kd, vd, causal=True, out=out, lse=lse, stream=s)
+        s.synchronize()
+        del b
+        O = out.float().cpu().numpy().astype(np.float64)
+        eo = max(max_err(O[0, h], refs[h]) for h in range(4))
+        assert eo <= TOL["bf16"][0], (how, eo)
