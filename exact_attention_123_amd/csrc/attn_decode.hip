@@ -78,11 +78,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_decode_kernel(
 
 // Merge of the splits: one wave per query row, D / 64 columns per lane.
 // The row's log-sum-exp over the splits, lse = ln sum_s exp(lse_s), comes
-// from wave reductions over lanes that each hold splits lane, lane + 64, ...;
-// then O = sum_s exp(lse_s - lse) O_s, with kCombineUnroll splits' partial rows
-// loaded at a time and each split's weight read from the lane that holds
-// it.  (A loop over the splits one load at a time is a chain of 3 nsplit
-// dependent memory round trips: 20 us for 32 splits.)
+// from wave reductions over lanes that each hold splits lane, lane + 64, ...
+// (the first 64 in a register, read once); then O = sum_s exp(lse_s - lse)
+// O_s, with kCombineUnroll splits' partial rows loaded at a time and each
+// split's weight read from the lane that holds it.  The first group of
+// partial rows is loaded before the reductions, which it does not depend
+// on, so that a merge of up to kCombineUnroll splits waits for one memory
+// round trip.  (A loop over the splits one load at a time is a chain of
+// 3 nsplit dependent memory round trips: 20 us for 32 splits.)
 constexpr int kCombineUnroll = 16;
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -104,28 +107,36 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // one per wave
   const int lane = threadIdx.x & 63;
   if (row >= NR) return;  // the whole wave
-  float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_lse[(size_t)s * NR + row]);
-  M = wave_max(M);
-  float L = 0.0f;
-  for (int s = lane; s < nsplit; s += 64)
-    L += exp2_hw((part_lse[(size_t)s * NR + row] - M) * kLog2e);
-  const float lse = M + log2_hw(wave_sum(L)) * kLn2;
-  float o[CPL] = {};
   const float* src = part_o + (size_t)row * D + lane * CPL;
   const size_t split_stride = (size_t)NR * D;
+  auto load = [&](float (&v)[kCombineUnroll][CPL], int s, int n) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k)
+#pragma unroll
+      for (int u = 0; u < CPL; ++u)
+        v[k][u] = k < n ? src[(size_t)(s + k) * split_stride + u] : 0.0f;
+  };
+  float v[kCombineUnroll][CPL];
+  load(v, 0, min(kCombineUnroll, nsplit));
+
+  const float x0 = lane < nsplit ? part_lse[(size_t)lane * NR + row] : -INFINITY;
+  float mx = x0;
+  for (int s = lane + 64; s < nsplit; s += 64) mx = fmaxf(mx, part_lse[(size_t)s * NR + row]);
+  const float M = wave_max(mx);
+  float L = exp2_hw((x0 - M) * kLog2e);  // exp2(-inf) = 0 past the last split
+  for (int s = lane + 64; s < nsplit; s += 64)
+    L += exp2_hw((part_lse[(size_t)s * NR + row] - M) * kLog2e);
+  const float lse = M + log2_hw(wave_sum(L)) * kLn2;
+
+  float o[CPL] = {};
   for (int s0 = 0; s0 < nsplit; s0 += 64) {
     // weight of split s0 + lane
     const int sl = s0 + lane;
-    const float w = sl < nsplit ? exp2_hw((part_lse[(size_t)sl * NR + row] - lse) * kLog2e) : 0.0f;
+    const float x = s0 == 0 ? x0 : sl < nsplit ? part_lse[(size_t)sl * NR + row] : -INFINITY;
+    const float w = exp2_hw((x - lse) * kLog2e);
     const int n = min(64, nsplit - s0);
     for (int i = 0; i < n; i += kCombineUnroll) {
-      float v[kCombineUnroll][CPL];
-#pragma unroll
-      for (int k = 0; k < kCombineUnroll; ++k)
-#pragma unroll
-        for (int u = 0; u < CPL; ++u)
-          v[k][u] = i + k < n ? src[(size_t)(s0 + i + k) * split_stride + u] : 0.0f;
+      if (s0 + i > 0) load(v, s0 + i, n - i);
 #pragma unroll
       for (int k = 0; k < kCombineUnroll; ++k) {
         // lanes i + k < 64 always (i < n <= 64, and the weight of a lane

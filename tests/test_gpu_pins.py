@@ -4,6 +4,7 @@ Several hold bitwise because of how the kernel computes: a masked score
 contributes exp2(-inf) = 0 exactly and never enters the running max, and
 every output column of an MFMA depends only on its own query's operand.
 """
+import gc
 import math
 import sys
 
@@ -195,14 +196,22 @@ def test_empty_and_stream_and_no_allocation():
         out.zero_()
         lse.zero_()
     torch.cuda.synchronize()
-    free0, _ = torch.cuda.mem_get_info()
-    alloc0 = torch.cuda.memory_allocated()
-    with torch.cuda.stream(s):
-        for _ in range(3):
-            ea.forward(qd, kd, vd, causal=True, out=out, lse=lse)
-    s.synchronize()
-    free1, _ = torch.cuda.mem_get_info()
-    assert torch.cuda.memory_allocated() == alloc0
+    # the collector stays off while the allocation counts are compared, so
+    # that no earlier test's tensors are freed in between
+    gc.collect()
+    gc.disable()
+    try:
+        free0, _ = torch.cuda.mem_get_info()
+        alloc0 = torch.cuda.memory_allocated()
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                ea.forward(qd, kd, vd, causal=True, out=out, lse=lse)
+        s.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        alloc1 = torch.cuda.memory_allocated()
+    finally:
+        gc.enable()
+    assert alloc1 == alloc0
     assert free1 == free0
     O = out.float().cpu().numpy().astype(np.float64)
     eo = 0.0

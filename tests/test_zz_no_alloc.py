@@ -9,6 +9,7 @@ bit-identical to attn_decode on the same inputs, and both are checked
 against the float64 decode oracle at the bf16 tolerances (2e-2 on O, 1e-3
 on LSE).  A problem whose split results exceed the scratch is rejected.
 """
+import gc
 import math
 import sys
 
@@ -44,13 +45,21 @@ def run_pair(B, H, Hkv, Tq, Tk, d, seed, causal=True):
     o = torch.full_like(q, float("nan"))
     lse = torch.full((B, H, Tq), float("nan"), dtype=torch.float32, device=q.device)
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
-    st = ea.attn_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                lse.data_ptr(), B, H, Hkv, Tq, Tk, Tk + 64, d, causal, scale,
-                                torch.cuda.current_stream().cuda_stream)
-    torch.cuda.synchronize()
+    # the collector stays off while the allocation count is compared, so
+    # that no earlier test's tensors are freed in between
+    gc.collect()
+    gc.disable()
+    try:
+        before = torch.cuda.memory_allocated()
+        st = ea.attn_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), B, H, Hkv, Tq, Tk, Tk + 64, d, causal, scale,
+                                    torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        after = torch.cuda.memory_allocated()
+    finally:
+        gc.enable()
     assert st == 0, ea.status_string(st)
-    assert torch.cuda.memory_allocated() == before
+    assert after == before
     assert torch.equal(o, o_ref) and torch.equal(lse, l_ref)
     O = o.float().cpu().numpy().astype(np.float64)
     L = lse.cpu().numpy().astype(np.float64)
