@@ -1052,6 +1052,13 @@ bool f32_rows(int64_t B, int64_t H, int64_t T, int64_t d) {
 // mask, d = 64 19.0 / 24.9.
 template <int D, int NW>
 constexpr bool kRowsKLds = D == 64 || NW == 4;
+// The software-pipelined block loop where a wave has its SIMD to itself
+// (d = 128, 4 waves, one workgroup per CU).  Measured on MI355X (us per
+// launch, pipelined / plain, bit-identical outputs): B H = 8, T = 2048,
+// causal, d = 128 25.7 / 27.6; the d = 64 instances, two workgroups per CU,
+// lose with it (d = 64 15.0 / 14.7).
+template <int D, int NW>
+constexpr bool kRowsPipe = D == 128 && NW == 4;
 
 // Square forward on the row-chunk kernel: Tq = Tk = T, one key split (the
 // chunk's keys are cut only between its NW waves), O and LSE written
@@ -1062,7 +1069,7 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 4 && D == 64 ? 2 : 1) void attn_fwd_rows_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int T, int G, int NR, int nwg, float c) {
-  attn_rows::row_chunk_attention<D, CAUSAL, NW, kRowsKLds<D, NW>>(
+  attn_rows::row_chunk_attention<D, CAUSAL, NW, kRowsKLds<D, NW>, kRowsPipe<D, NW>>(
       Q, K, V, O, LSE, nullptr, nullptr, T, T, T, G, 1, T, NR, nwg, c);
 }
 

@@ -57,7 +57,10 @@ constexpr int kMaxRows = 32;  // query rows of one workgroup (one MFMA column bl
 // costs the vector memory pipeline four times the work of a coalesced load:
 // the right trade when the kernel streams a long cache from HBM (decode),
 // not when it re-reads short key ranges from L2 (forward on small grids).
-template <int D, bool CAUSAL, int NW = kWaves, bool KLDS = false>
+// PIPE: software-pipelined block loop (see below), for instances with one
+// wave per SIMD, whose own chain no other wave hides; with two waves per
+// SIMD the plain loop is as fast and needs fewer registers.
+template <int D, bool CAUSAL, int NW = kWaves, bool KLDS = false, bool PIPE = false>
 __device__ __forceinline__ void row_chunk_attention(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ part_o,
@@ -133,10 +136,11 @@ __device__ __forceinline__ void row_chunk_attention(
   // K operand of lane (j, h): row row_perm(j) of the block, d from
   // 8 NDS h on (see qf).  Keys >= k_hi read as zero (and are masked below).
   const int krow = row_perm(j) * RB + 16 * NDS * h;
-  auto load = [&](bf16x8_t (&kr)[NDS], char* kt, char* vt, int i) __attribute__((always_inline)) {
+  // Loads of the wave's i-th block (keys kb0 ..): K into registers kr or
+  // LDS stage kt, V into LDS stage vt.  (No load into a stage may move
+  // above the reads of the block that stage held before.)
+  auto load_k = [&](bf16x8_t (&kr)[NDS], char* kt, int i) __attribute__((always_inline)) {
     const int kb0 = k_lo + kBlk * (wave + NW * i);
-    // (no load of the next block may move above the reads of the previous
-    // one from the same stage)
     asm volatile("" ::: "memory");
     if constexpr (KLDS) {
       dma.load(kt, Kh, k_hi, kb0, 0);
@@ -147,7 +151,10 @@ __device__ __forceinline__ void row_chunk_attention(
       for (int s = 0; s < NDS; ++s)
         kr[s] = __builtin_bit_cast(bf16x8_t, buf_load16(rk, krow + 16 * s));
     }
-    dma.load(vt, Vh, k_hi, kb0, 0);
+  };
+  auto load_v = [&](char* vt, int i) __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    dma.load(vt, Vh, k_hi, k_lo + kBlk * (wave + NW * i), 0);
   };
 
   f32x16_t oacc[NDT];
@@ -156,17 +163,22 @@ __device__ __forceinline__ void row_chunk_attention(
   float m_run = kMinusHuge, l_run = 0.0f, w_run = 0.0f;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // One block: scores, mask, online softmax, O^T += V^T P^T.
-  auto block = [&](const bf16x8_t (&kr)[NDS], const char* kt, const char* vt, int i)
+  // The steps of one block (keys kb0 ..):
+  // scores S^T = K Q^T;
+  auto qk = [&](const bf16x8_t (&kr)[NDS], const char* kt, f32x16_t& sc)
       __attribute__((always_inline)) {
-    const int kb0 = k_lo + kBlk * (wave + NW * i);
-    f32x16_t sc = f32x16_t{};
+    sc = f32x16_t{};
 #pragma unroll
     for (int s = 0; s < NDS; ++s)
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(KLDS ? lds_row(kt, ad.row[s]) : kr[s], qf[s],
                                                    sc, 0, 0, 0);
-    // scores in log2 units (any sign of the scale); register 8 a + e holds
-    // key kb0 + 16 a + 8 h + e of query row j
+  };
+  // the scores in log2 units (any sign of the scale; register 8 a + e holds
+  // key kb0 + 16 a + 8 h + e of query row j), the mask, the row max and,
+  // where it outgrew the running max by more than the threshold, the
+  // rescaling of the accumulator and normalisers;
+  auto rescale = [&](f32x16_t& sc, int i) __attribute__((always_inline)) {
+    const int kb0 = k_lo + kBlk * (wave + NW * i);
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] *= c;
     if (kb0 + kBlk > k_hi || (CAUSAL && kb0 + kBlk > k_all)) {
@@ -191,7 +203,9 @@ __device__ __forceinline__ void row_chunk_attention(
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
       m_run = grow ? mt : m_run;
     }
-    bf16x8_t pb[2];
+  };
+  // the weights and their bf16 rounding, with both normalisers;
+  auto weights = [&](const f32x16_t& sc, bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -211,12 +225,17 @@ __device__ __forceinline__ void row_chunk_attention(
                                              w_run, false);
       w_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[a], pb[a], 6, 7), one2,
                                              w_run, false);
+    }
+  };
+  // O^T += V^T P^T.
+  auto pv = [&](const char* vt, const bf16x8_t (&pb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             lds_tr(vt, 16 * a * RB + ad.tr[0][dt], 16 * a * RB + ad.tr[1][dt]), pb[a],
             oacc[dt], 0, 0, 0);
-    }
   };
   // Waits until at most n of this wave's loads are in flight (loads
   // complete in issue order; a direct-to-LDS load has written LDS when it
@@ -227,30 +246,110 @@ __device__ __forceinline__ void row_chunk_attention(
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
     asm volatile("" ::: "memory");
   };
+  constexpr int PERK = KLDS ? PER : NDS;  // load instructions of one K block
   using Zero = std::integral_constant<int, 0>;
-  // one block's loads
-  using Next = std::integral_constant<int, KLDS ? 2 * PER : NDS + PER>;
+  using WaitV = std::integral_constant<int, PER>;
+  using WaitKV = std::integral_constant<int, PER + PERK>;
 
   bf16x8_t k0[NDS], k1[NDS];
+#pragma unroll
+  for (int s = 0; s < NDS; ++s) k0[s] = k1[s] = bf16x8_t{};
   char* kt0 = KLDS ? sK0[KLDS ? wave : 0] : nullptr;
   char* kt1 = KLDS ? sK1[KLDS ? wave : 0] : nullptr;
-  if (nmine > 0) load(k0, kt0, sV0[wave], 0);
-  for (int i = 0; i < nmine; i += 2) {
-    if (i + 1 < nmine) {
-      load(k1, kt1, sV1[wave], i + 1);
-      wait_loads(Next{});
-    } else {
-      wait_loads(Zero{});
+  if constexpr (!PIPE) {
+    // Plain loop: block i's K and V in stage i % 2, the next block's loads
+    // issued before the block's steps run one after the other.
+    auto block = [&](const bf16x8_t (&kr)[NDS], const char* kt, const char* vt, int i)
+        __attribute__((always_inline)) {
+      f32x16_t sc;
+      bf16x8_t pb[2];
+      qk(kr, kt, sc);
+      rescale(sc, i);
+      weights(sc, pb);
+      pv(vt, pb);
+    };
+    if (nmine > 0) {
+      load_k(k0, kt0, 0);
+      load_v(sV0[wave], 0);
     }
-    block(k0, kt0, sV0[wave], i);
-    if (i + 1 >= nmine) break;
-    if (i + 2 < nmine) {
-      load(k0, kt0, sV0[wave], i + 2);
-      wait_loads(Next{});
-    } else {
-      wait_loads(Zero{});
+    for (int i = 0; i < nmine; i += 2) {
+      if (i + 1 < nmine) {
+        load_k(k1, kt1, i + 1);
+        load_v(sV1[wave], i + 1);
+        wait_loads(WaitKV{});
+      } else {
+        wait_loads(Zero{});
+      }
+      block(k0, kt0, sV0[wave], i);
+      if (i + 1 >= nmine) break;
+      if (i + 2 < nmine) {
+        load_k(k0, kt0, i + 2);
+        load_v(sV0[wave], i + 2);
+        wait_loads(WaitKV{});
+      } else {
+        wait_loads(Zero{});
+      }
+      block(k1, kt1, sV1[wave], i + 1);
     }
-    block(k1, kt1, sV1[wave], i + 1);
+  } else {
+    // Software pipeline over the wave's blocks, two stages each of K and V:
+    // step i issues V_i and K_{i+2}, then (once K_{i+1} and V_{i-1} have
+    // landed) accumulates P_{i-1} V_{i-1} while it takes the row max of S_i,
+    // and computes S_{i+1} while it takes the weights of S_i, so that each
+    // wave's matrix work overlaps its own softmax.  Block i uses K stage i % 2
+    // and V stage i % 2; score tiles and weights alternate between the X
+    // (even i) and Y (odd i) registers.  At the last step S_{i+1} comes from
+    // a stage that holds no new block and is never used.
+    f32x16_t sX, sY;
+    bf16x8_t pX[2], pY[2];
+    auto step = [&](auto odd, int i) __attribute__((always_inline)) {
+      constexpr bool O = decltype(odd)::value;  // i % 2
+      char* vfree = O ? sV1[wave] : sV0[wave];  // V_i's stage (V_{i-2} read at step i - 1)
+      const char* vprev = O ? sV0[wave] : sV1[wave];
+      if (i + 2 < nmine) {
+        load_v(vfree, i);
+        load_k(O ? k1 : k0, O ? kt1 : kt0, i + 2);  // K_i's stage, read at step i - 1
+        wait_loads(WaitKV{});
+      } else {
+        load_v(vfree, i);
+        wait_loads(WaitV{});
+      }
+      pv(vprev, O ? pX : pY);
+      rescale(O ? sY : sX, i);
+      qk(O ? k0 : k1, O ? kt0 : kt1, O ? sX : sY);
+      weights(O ? sY : sX, O ? pY : pX);
+    };
+    using Even = std::false_type;
+    using Odd = std::true_type;
+    if (nmine > 0) {
+      load_k(k0, kt0, 0);
+      if (nmine > 1) {
+        load_k(k1, kt1, 1);
+        wait_loads(std::integral_constant<int, PERK>{});
+      } else {
+        wait_loads(Zero{});
+      }
+      qk(k0, kt0, sX);
+      // step 0, with no P V yet: V_0 and K_2 (into K_0's stage, which S_0 has
+      // read), then S_1 once K_1 has landed
+      load_v(sV0[wave], 0);
+      if (nmine > 2) {
+        load_k(k0, kt0, 2);
+        wait_loads(WaitKV{});
+      } else {
+        wait_loads(WaitV{});
+      }
+      rescale(sX, 0);
+      qk(k1, kt1, sY);
+      weights(sX, pX);
+      for (int i = 1; i < nmine; i += 2) {
+        step(Odd{}, i);
+        if (i + 1 >= nmine) break;
+        step(Even{}, i + 1);
+      }
+      wait_loads(Zero{});
+      pv((nmine & 1) ? sV0[wave] : sV1[wave], (nmine & 1) ? pX : pY);
+    }
   }
 
   // Merge the waves' partial results for each query row.

@@ -11,6 +11,9 @@ each first asserting by name which instance its sizes select:
   - the row-chunk forward with 8 waves at d = 128 without a mask (grids
     below the CU count with T >= 4096); output against the float64 oracle
     at the bf16 tolerances;
+  - the row-chunk forward with 4 waves at d = 128 (its software-pipelined
+    block loop) for every count of 32-key blocks per wave from 0 to 9,
+    both masks, every row against the float64 oracle;
   - the matrix-core probe (both MFMA shapes): the sum of a wave's sink
     values equals, in closed form, the number of trips times the sum of
     all outputs of the wave's MFMAs, and the sum of all outputs of one MFMA
@@ -91,6 +94,41 @@ def test_rows_w8_d128_full(T):
         el = float(np.abs(L[0, h, rows] - ref["LSE"]).max())
         say(f"    head {h}: max|O err|={eo:.3e} max|LSE err|={el:.3e}")
         assert eo <= 2e-2 and el <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Row-chunk forward, 4 waves, d = 128 (software-pipelined block loop)
+# ---------------------------------------------------------------------------
+
+# Wave w of a chunk takes the chunk's 32-key blocks w, w + 4, ...: these
+# lengths give the waves 0 .. 9 blocks each (ragged last blocks included).
+ROWS_W4_T = [1, 31, 32, 33, 64, 96, 127, 128, 129, 160, 161, 255, 256, 300, 640, 1000, 1100]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("T", ROWS_W4_T)
+def test_rows_w4_d128_block_counts(T, causal):
+    import torch
+
+    import exact_attention_123_amd as ea
+    B, H, d = 1, 2, 128
+    name = ea.fwd_kernel_name_for(B, H, T, d, causal)
+    mask = "causal" if causal else "full"
+    assert name == f"attn_fwd_rows_bf16_d128_{mask}_br32_bc32_w4", name
+    say(f"[rows w4 d128] {name} T={T}")
+    x = make_qkv(B, H, T, d, dtype="bf16", seed=9450 + T, qk_mult=2.0)
+    q, k, v = (to_device(a, "bf16") for a in (x.q, x.k, x.v))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = ea.forward(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    O = o.float().cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    for h in range(H):
+        ref = oracle.attention_head(x.q64(0, h), x.k64(0, h), x.v64(0, h), causal=causal,
+                                    scale=scale)
+        eo = float(np.abs(O[0, h] - ref["O"]).max())
+        el = float(np.abs(L[0, h] - ref["LSE"]).max())
+        assert eo <= 2e-2 and el <= 1e-3, (h, eo, el)
 
 
 # ---------------------------------------------------------------------------
