@@ -18,14 +18,18 @@
 //             scale, or -LSE_i log2(e)) per query row, into the caller's
 //             workspace.
 //   2. dkdv : one workgroup of 8 waves per 256 keys of a head (32 per
-//             wave; 4 waves per 128 keys when the 256-key blocks of the
-//             problem are fewer than the device's CUs), K of those keys
-//             staged in LDS and V held in registers; it walks 64-query
-//             tiles of Q and dO (staged in LDS) and accumulates
-//             dV^T += dO^T P and dK^T += Q^T dS in registers.
+//             wave), K of those keys staged in LDS and V held in
+//             registers; it walks 64-query tiles of Q and dO (staged in
+//             LDS) and accumulates dV^T += dO^T P and dK^T += Q^T dS in
+//             registers.  When the 256-key blocks of the problem are fewer
+//             than the device's CUs: 128 keys per workgroup, two waves per
+//             32 keys, each taking one half of every query tile, their sums
+//             added at the end.
 //   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
 //             registers; it walks 64-key tiles of K and V (staged in LDS)
-//             and accumulates dQ^T += K^T dS^T.
+//             and accumulates dQ^T += K^T dS^T.  When the 128-query blocks
+//             are fewer than the CUs: two waves per 32 queries, each taking
+//             one half of every key tile.
 // dkdv and dq each recompute S and dP for their tiles; neither needs
 // atomics or a second pass, and every output element is written by exactly
 // one lane (the result does not depend on scheduling).
@@ -51,11 +55,11 @@ using attn_internal::device_cus;
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
-// dkdv: 32 keys per wave; 8 waves (256 keys) per workgroup, or 4 waves
-// (128 keys) when the 256-key blocks would be fewer than the device's CUs
+// dkdv: 8 waves per workgroup, 32 keys per wave (256 keys), or two waves
+// per 32 keys (128 keys) when the 256-key blocks would be fewer than the
+// device's CUs
 constexpr int kDkdvWaves = 8;
-constexpr int kDkdvWavesSmall = 4;
-constexpr int kBK = 32 * kDkdvWaves;  // keys per dkdv workgroup (8 waves)
+constexpr int kBK = 32 * kDkdvWaves;  // keys per dkdv workgroup (unpaired)
 constexpr int kBQ = 128;       // queries per dq workgroup
 constexpr int kTile = 64;      // rows of a staged Q/dO (dkdv) or K/V (dq) tile
 // Heads an XCD works on side by side in the dq kernel (see its workgroup
@@ -108,21 +112,27 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(
 // accumulator.  The fp32 error of the folded exponent is about 2^-24
 // |LSE log2(e)|, against 2^-9 for the bf16 rounding of P that follows.
 //
-// NW = 8 waves, two per SIMD (at most 256 registers per lane, so that the
+// 8 waves, two per SIMD (at most 256 registers per lane, so that the
 // matrix results stay in VGPRs where the softmax reads them): the block's
 // 256 keys are staged in LDS once, each wave holds V of its 32 keys and
 // its dK, dV accumulators in registers, and the staged Q and dO tiles serve
-// all 256 keys.  NW = 4 (128 keys, one wave per SIMD) for problems with
+// all 256 keys.  PAIR (128 keys, two waves per 32 keys) for problems with
 // fewer 256-key blocks than CUs: there the heaviest block's walk over every
-// query tile sets the time, and a 128-key block halves it.
-template <int D, bool CAUSAL, bool FOLD, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
+// query tile sets the time; a 128-key block halves the walk and the pair's
+// split of every tile halves each wave's share again.  Measured on MI355X
+// (us per call of the whole backward, paired / 4 waves of 32 keys per
+// 128-key block, dQ likewise paired / not): B H = 8, T = 2048, causal,
+// d = 64 65.0 / 83.0, d = 128 99.9 / 119.9; no mask, d = 64 64.2 / 82.7;
+// B H = 8, T = 4096, d = 128 199.8 / 225.0.
+template <int D, bool CAUSAL, bool FOLD, bool PAIR>
+__global__ __launch_bounds__(64 * kDkdvWaves, 1) void attn_bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dK,
     __bf16* __restrict__ dV, int T, int BHkv, int G, int nkb, float c, float scale) {
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
-  constexpr int BK = 32 * NW;  // keys per workgroup
+  constexpr int NW = kDkdvWaves;
+  constexpr int BK = PAIR ? 16 * NW : 32 * NW;  // keys per workgroup
 
   // Two stages, each operand and stage its own object: the compiler then
   // tells the direct-to-LDS loads into one stage from the reads of the
@@ -167,10 +177,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
     bhkv = id % BHkv;
   }
   const size_t head = (size_t)bhkv * (size_t)T * D;
-  // With 8 waves, waves w and w + 4 share a SIMD; they take key groups w
-  // and 7 - w, so that under a causal mask every SIMD skips the same number
-  // of sub-tiles on the diagonal.
-  const int kg = NW == 8 ? (wave < 4 ? wave : 11 - wave) : wave;
+  // Waves w and w + 4 share a SIMD; they take key groups w and 7 - w (256
+  // keys) or w and 3 - w (PAIR: 128 keys, each group's two waves taking
+  // the first (w < 4) and the second 32 queries of every staged tile), so
+  // that under a causal mask every SIMD skips the same number of sub-tiles
+  // on the diagonal.
+  const int kg = wave < 4 ? wave : (PAIR ? 7 : 11) - wave;
+  const int u_mine = wave >> 2;  // PAIR: the wave's half of each tile
   const int k0 = kb * BK, kw0 = k0 + 32 * kg;
   const int64_t n = (int64_t)BHkv * G * T;
 
@@ -253,6 +266,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
       const int i0 = qt * kTile + 32 * u;
       if (st) stage(nq, ng, nl, nd, nm, nq_t, u);
       __builtin_amdgcn_sched_barrier(0);
+      if (PAIR && u != u_mine) continue;
       // Nothing to add when every query of the sub-tile precedes every key
       // of the wave (causal) or lies past the end of the sequence (its Q
       // and dO rows read as zero).  Without a branch here the non-causal
@@ -377,6 +391,33 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
     r = rn, m = mn;
   }
 
+  if constexpr (PAIR) {
+    // The two waves of a key group add their sums, the second half's into
+    // the first's (a fixed order), through the stages, which every wave is
+    // done with (the walk ends at a barrier): one stage of 64 lanes x 16 NDT
+    // floats per group, dK then dV.
+    static_assert(C::TBYTES == NDT * 16 * 64 * 4, "merge buffer");
+    float* buf = reinterpret_cast<float*>(kg == 0 ? sQ0 : kg == 1 ? sQ1 : kg == 2 ? sG0 : sG1);
+    auto merge = [&](f32x16_t (&acc)[NDT]) __attribute__((always_inline)) {
+      if (u_mine == 1) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) buf[(16 * dt + r) * 64 + lane] = acc[dt][r];
+      }
+      __syncthreads();
+      if (u_mine == 0) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] += buf[(16 * dt + r) * 64 + lane];
+      }
+      __syncthreads();
+    };
+    merge(dk);
+    merge(dv);
+    if (u_mine == 1) return;
+  }
   store_rows<D>(dK + head, dk, scale, kw0 + j, T, h);
   store_rows<D>(dV + head, dv, 1.0f, kw0 + j, T, h);
 }
@@ -384,13 +425,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 // 3. dq
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ ws, __bf16* __restrict__ dQ, int T,
-    int BH, int nqb, int G, float c, float cw, float scale) {
+// PAIR: 8 waves, two per 32 queries, taking the first (waves 0-3) and the
+// second 32 keys of every staged tile; for grids with fewer workgroups than
+// CUs, where the heaviest block's walk over every key tile sets the time.
+template <int D, bool CAUSAL, bool PAIR>
+__global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void
+attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                   const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
+                   const float* __restrict__ ws, __bf16* __restrict__ dQ, int T, int BH, int nqb,
+                   int G, float c, float cw, float scale) {
   using C = BwdTile<D>;
   constexpr int NDS = C::NDS, NDT = C::NDT, RB = C::RB;
+  constexpr int NW = PAIR ? 2 * kWaves : kWaves;
 
   // Two stages, each operand and stage its own object (see the dK/dV kernel).
   __shared__ __attribute__((aligned(1024))) char sK0[C::TBYTES];
@@ -400,6 +446,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & (kWaves - 1);  // the wave's 32 queries
+  const int u_mine = wave >> 2;        // PAIR: the wave's half of each tile
   const int j = lane & 31, h = lane >> 5;
   // Heavy-first: the last query blocks see the most key tiles.  Head slot
   // hid is member hid / NKV of key/value group hid % NKV, so that the query
@@ -422,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
   const int nkv = BH / G, bhkv = hid % nkv, bh = bhkv * G + hid / nkv;
   const size_t head = (size_t)bh * (size_t)T * D;
   const size_t kvhead = (size_t)bhkv * (size_t)T * D;
-  const int q0 = qb * kBQ, qw0 = q0 + 32 * wave, qg = qw0 + j;
+  const int q0 = qb * kBQ, qw0 = q0 + 32 * rg, qg = qw0 + j;
   const int64_t n = (int64_t)BH * T;
 
   // Q and dO of the wave's 32 queries: B operands [d][query] of S^T = K Q^T
@@ -451,7 +499,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 
   TileAddr<D> ad;
   ad.init(lane);
-  TileDma<D, kTile, kWaves> dma;
+  TileDma<D, kTile, NW> dma;
   dma.init(wave, lane);
   auto stage = [&](char* tk, char* tv, int t) __attribute__((always_inline)) {
     dma.load(tk, K + kvhead, T, t * kTile, wave);
@@ -469,6 +517,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int kv0 = t * kTile + 32 * u;
+      if (PAIR && u != u_mine) continue;
       // every key of the sub-tile follows every query of the wave
       if (CAUSAL && kv0 > qw0 + 31) continue;
       f32x16_t S = f32x16_t{}, dP = dP0;
@@ -532,6 +581,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  if constexpr (PAIR) {
+    // The two waves of 32 queries add their sums, the second half's into
+    // the first's (a fixed order), through the stages, which every wave is
+    // done with (the walk ends at a barrier): one stage of 64 lanes x 16 NDT
+    // floats per query group.
+    static_assert(C::TBYTES == NDT * 16 * 64 * 4, "merge buffer");
+    float* buf = reinterpret_cast<float*>(rg == 0 ? sK0 : rg == 1 ? sK1 : rg == 2 ? sV0 : sV1);
+    if (u_mine == 1) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) buf[(16 * dt + r) * 64 + lane] = dq[dt][r];
+    }
+    __syncthreads();
+    if (u_mine == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq[dt][r] += buf[(16 * dt + r) * 64 + lane];
+  }
   store_rows<D>(dQ + head, dq, scale, qg, T, h);
 }
 
@@ -545,31 +614,41 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-template <int D, bool FOLD, int NW>
+template <int D, bool FOLD, bool PAIR>
 const void* dkdv_kernel(int causal) {
-  return causal ? (const void*)attn_bwd_dkdv_kernel<D, true, FOLD, NW>
-                : (const void*)attn_bwd_dkdv_kernel<D, false, FOLD, NW>;
+  return causal ? (const void*)attn_bwd_dkdv_kernel<D, true, FOLD, PAIR>
+                : (const void*)attn_bwd_dkdv_kernel<D, false, FOLD, PAIR>;
 }
-template <int D, int NW>
+template <int D, bool PAIR>
 const void* dkdv_kernel(int causal, bool fold) {
-  return fold ? dkdv_kernel<D, true, NW>(causal) : dkdv_kernel<D, false, NW>(causal);
+  return fold ? dkdv_kernel<D, true, PAIR>(causal) : dkdv_kernel<D, false, PAIR>(causal);
 }
 template <int D>
-const void* dkdv_kernel(int causal, bool fold, int nw) {
-  return nw == kDkdvWavesSmall ? dkdv_kernel<D, kDkdvWavesSmall>(causal, fold)
-                               : dkdv_kernel<D, kDkdvWaves>(causal, fold);
+const void* dkdv_kernel(int causal, bool fold, bool pair) {
+  return pair ? dkdv_kernel<D, true>(causal, fold) : dkdv_kernel<D, false>(causal, fold);
 }
 
-// Waves per dK/dV workgroup for these sizes: 4 when the 256-key blocks of
-// all key/value heads are fewer than the CUs, else 8.
-int dkdv_waves(int64_t BHkv, int64_t T) {
-  return BHkv * ((T + kBK - 1) / kBK) < device_cus() ? kDkdvWavesSmall : kDkdvWaves;
+// Paired waves (128 keys per workgroup, two waves per 32 keys) when the
+// 256-key blocks of all key/value heads are fewer than the CUs: there the
+// heaviest block's walk over every query tile sets the time, and a
+// 128-key block with the tiles' halves split between two waves shortens
+// each wave's walk to a quarter.
+bool dkdv_paired(int64_t BHkv, int64_t T) {
+  return BHkv * ((T + kBK - 1) / kBK) < device_cus();
+}
+template <int D, bool PAIR>
+const void* dq_kernel(int causal) {
+  return causal ? (const void*)attn_bwd_dq_kernel<D, true, PAIR>
+                : (const void*)attn_bwd_dq_kernel<D, false, PAIR>;
 }
 template <int D>
-const void* dq_kernel(int causal) {
-  return causal ? (const void*)attn_bwd_dq_kernel<D, true>
-                : (const void*)attn_bwd_dq_kernel<D, false>;
+const void* dq_kernel(int causal, bool pair) {
+  return pair ? dq_kernel<D, true>(causal) : dq_kernel<D, false>(causal);
 }
+
+// Paired waves in the dQ kernel (8 per 128 queries) when its 128-query
+// blocks are fewer than the CUs.
+bool dq_paired(int64_t BH, int64_t T) { return BH * ((T + kBQ - 1) / kBQ) < device_cus(); }
 
 }  // namespace
 
@@ -634,15 +713,16 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
                *gb = (const __bf16*)dout;
   const float* wsc = ws;
   {
-    const int nw = dkdv_waves(BHkv, T);
-    int nkb = (int)((T + 32 * nw - 1) / (32 * nw));
+    const bool pair = dkdv_paired(BHkv, T);
+    const int bk = pair ? kBK / 2 : kBK;
+    int nkb = (int)((T + bk - 1) / bk);
     __bf16 *dkb = (__bf16*)dk, *dvb = (__bf16*)dv;
     void* args[] = {(void*)&qb,  (void*)&kb_, (void*)&vb, (void*)&gb,  (void*)&wsc,
                     (void*)&dkb, (void*)&dvb, (void*)&t,  (void*)&bhkv, (void*)&g,
                     (void*)&nkb, (void*)&c,   (void*)&scale};
     const void* kern =
-        d == 64 ? dkdv_kernel<64>(causal, fold, nw) : dkdv_kernel<128>(causal, fold, nw);
-    if (hipLaunchKernel(kern, dim3((unsigned)(bhkv * nkb)), dim3(64 * nw), args, 0,
+        d == 64 ? dkdv_kernel<64>(causal, fold, pair) : dkdv_kernel<128>(causal, fold, pair);
+    if (hipLaunchKernel(kern, dim3((unsigned)(bhkv * nkb)), dim3(64 * kDkdvWaves), args, 0,
                         stream) !=
         hipSuccess)
       return ATTN_ERR_LAUNCH;
@@ -653,9 +733,10 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     void* args[] = {(void*)&qb, (void*)&kb_, (void*)&vb,  (void*)&gb, (void*)&wsc,
                     (void*)&dqb, (void*)&t,  (void*)&bh,  (void*)&nqb, (void*)&g,
                     (void*)&c,  (void*)&cw, (void*)&scale};
-    const void* kern = d == 64 ? dq_kernel<64>(causal) : dq_kernel<128>(causal);
-    if (hipLaunchKernel(kern, dim3((unsigned)(bh * nqb)), dim3(kThreads), args, 0, stream) !=
-        hipSuccess)
+    const bool pair = dq_paired(BH, T);
+    const void* kern = d == 64 ? dq_kernel<64>(causal, pair) : dq_kernel<128>(causal, pair);
+    if (hipLaunchKernel(kern, dim3((unsigned)(bh * nqb)), dim3(pair ? 2 * kThreads : kThreads),
+                        args, 0, stream) != hipSuccess)
       return ATTN_ERR_LAUNCH;
   }
   return ATTN_OK;
@@ -689,12 +770,22 @@ const char* attn_bwd_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t
   if (B <= 0 || H <= 0 || H_kv <= 0 || T <= 0 || H % H_kv != 0) return nullptr;
   const char* name = attn_bwd_kernel_name(d, causal, which);
   if (name == nullptr || check_device() != ATTN_OK) return nullptr;
-  if (which != 1 || dkdv_waves(B * H_kv, T) == kDkdvWaves) return name;
-  static const char* small[2][2] = {
-      {"attn_bwd_dkdv_bf16_d64_full_bk128_bq64_w4", "attn_bwd_dkdv_bf16_d64_causal_bk128_bq64_w4"},
-      {"attn_bwd_dkdv_bf16_d128_full_bk128_bq64_w4",
-       "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4"}};
-  return small[d == 128 ? 1 : 0][causal];
+  if (which == 1 && dkdv_paired(B * H_kv, T)) {
+    static const char* small[2][2] = {
+        {"attn_bwd_dkdv_bf16_d64_full_bk128_bq64_w8",
+         "attn_bwd_dkdv_bf16_d64_causal_bk128_bq64_w8"},
+        {"attn_bwd_dkdv_bf16_d128_full_bk128_bq64_w8",
+         "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w8"}};
+    return small[d == 128 ? 1 : 0][causal];
+  }
+  if (which == 2 && dq_paired(B * H, T)) {
+    static const char* small[2][2] = {
+        {"attn_bwd_dq_bf16_d64_full_bq128_bk64_w8", "attn_bwd_dq_bf16_d64_causal_bq128_bk64_w8"},
+        {"attn_bwd_dq_bf16_d128_full_bq128_bk64_w8",
+         "attn_bwd_dq_bf16_d128_causal_bq128_bk64_w8"}};
+    return small[d == 128 ? 1 : 0][causal];
+  }
+  return name;
 }
 
 }  // extern "C"

@@ -176,9 +176,12 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
  * launches for these sizes on the current device, to inspect the instance
  * actually selected ("FlashAttention -- avoid writing the giant
  * intermediate", "Apply it at the right layer").  The dK/dV kernel takes
- * 256-key workgroups of 8 waves, or 128-key workgroups of 4 waves
- * ("attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w4") when B * H_kv * ceil(T /
- * 256) is below the device's CU count.  NULL for unsupported or
+ * 256-key workgroups of 8 waves, or, when B * H_kv * ceil(T / 256) is below
+ * the device's CU count, 128-key workgroups of 8 waves, two per 32 keys
+ * ("attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w8"); the dQ kernel takes
+ * 128-query workgroups of 4 waves, or, when B * H * ceil(T / 128) is below
+ * the CU count, of 8 waves, two per 32 queries
+ * ("attn_bwd_dq_bf16_d128_causal_bq128_bk64_w8").  NULL for unsupported or
  * non-positive sizes, or when the current device is not a gfx950.
  */
 const char* attn_bwd_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t T, int64_t d,

@@ -1,10 +1,13 @@
-"""GPU parity of the dK/dV kernel's two instances.
+"""GPU parity of the dK/dV and dQ kernels' two instances each.
 
-The backward's dK/dV kernel takes 256-key workgroups of 8 waves, or 128-key
-workgroups of 4 waves when the 256-key blocks of all key/value heads are
-fewer than the device's CUs.  Each case asserts the instance first, then
-checks sampled (or all) rows and keys of some heads against the float64
-oracle under the per-element bound of the backward tests.
+The backward's dK/dV kernel takes 256-key workgroups of 8 waves (32 keys
+each), or 128-key workgroups of 8 waves, two per 32 keys splitting every
+query tile, when the 256-key blocks of all key/value heads are fewer than
+the device's CUs.  The dQ kernel takes 128-query workgroups of 4 waves, or
+of 8 waves, two per 32 queries splitting every key tile, when its 128-query
+blocks are fewer than the CUs.  Each case asserts both instances first,
+then checks sampled (or all) rows and keys of some heads against the
+float64 oracle under the per-element bound of the backward tests.
 """
 import math
 import sys
@@ -28,20 +31,25 @@ def cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
-# (B, H, T, d): grids below and above the switch on a 256-CU device
+# (B, H, T, d): grids below and above the switches on a 256-CU device
+# (B H = 16, T = 2048: paired dK/dV, unpaired dQ; T = 100: one block, its
+# second 32 rows past the end)
 CASES = [(1, 8, 2048, 64), (1, 8, 2048, 128), (2, 3, 700, 128), (1, 1, 5000, 64),
-         (1, 32, 2048, 128), (2, 16, 2048, 64)]
+         (1, 32, 2048, 128), (2, 16, 2048, 64), (1, 16, 2048, 64), (1, 2, 100, 128),
+         (3, 1, 33, 64)]
 
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 @pytest.mark.parametrize("B,H,T,d", CASES)
-def test_dkdv_instances(B, H, T, d, causal):
+def test_bwd_instances(B, H, T, d, causal):
     import exact_attention_123_amd as ea
     name = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 1)
     small = B * H * ((T + 255) // 256) < cus()
-    want = "bk128_bq64_w4" if small else "bk256_bq64_w8"
-    assert name.endswith(want), name
-    say(f"[bwd instance] {name} B={B} H={H} T={T}")
+    assert name.endswith("bk128_bq64_w8" if small else "bk256_bq64_w8"), name
+    qname = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 2)
+    qsmall = B * H * ((T + 127) // 128) < cus()
+    assert qname.endswith("bq128_bk64_w8" if qsmall else "bq128_bk64_w4"), qname
+    say(f"[bwd instance] {name} {qname} B={B} H={H} T={T}")
     scale = 1.0 / math.sqrt(d)
     x = make_qkv(B, H, T, d, seed=8100 + T + d + H, qk_mult=2.0)
     do = make_dout(B, H, T, d, seed=8200 + T + d)
