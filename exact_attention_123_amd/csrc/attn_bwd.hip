@@ -28,8 +28,8 @@
 //   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
 //             registers; it walks 64-key tiles of K and V (staged in LDS)
 //             and accumulates dQ^T += K^T dS^T.  When the 128-query blocks
-//             are fewer than the CUs: two waves per 32 queries, each taking
-//             one half of every key tile.
+//             are fewer than twice the CUs: two waves per 32 queries, each
+//             taking one half of every key tile.
 // dkdv and dq each recompute S and dP for their tiles; neither needs
 // atomics or a second pass, and every output element is written by exactly
 // one lane (the result does not depend on scheduling).
@@ -426,8 +426,9 @@ __global__ __launch_bounds__(64 * kDkdvWaves, 1) void attn_bwd_dkdv_kernel(
 // 3. dq
 // ---------------------------------------------------------------------------
 // PAIR: 8 waves, two per 32 queries, taking the first (waves 0-3) and the
-// second 32 keys of every staged tile; for grids with fewer workgroups than
-// CUs, where the heaviest block's walk over every key tile sets the time.
+// second 32 keys of every staged tile; for grids of fewer workgroups than
+// twice the CUs, where the heaviest block's walk over every key tile sets
+// the time.
 template <int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void
 attn_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -647,8 +648,15 @@ const void* dq_kernel(int causal, bool pair) {
 }
 
 // Paired waves in the dQ kernel (8 per 128 queries) when its 128-query
-// blocks are fewer than the CUs.
-bool dq_paired(int64_t BH, int64_t T) { return BH * ((T + kBQ - 1) / kBQ) < device_cus(); }
+// blocks are fewer than twice the CUs (the unpaired kernel's two
+// workgroups per CU).  Measured on MI355X (us per call of the backward,
+// paired below 2 / 1 CU count): B H = 16, T = 2048, causal, d = 64
+// 65.9 / 70.8, d = 128 103.5 / 111.7; B H = 8, T = 4096, d = 128
+// 183.7 / 201.4; B H = 24, T = 2048, d = 128 131.7 / 140.2; the same at
+// 512 blocks and more, where neither pairs.
+bool dq_paired(int64_t BH, int64_t T) {
+  return BH * ((T + kBQ - 1) / kBQ) < 2 * device_cus();
+}
 
 }  // namespace
 

@@ -5,7 +5,7 @@ each), or 128-key workgroups of 8 waves, two per 32 keys splitting every
 query tile, when the 256-key blocks of all key/value heads are fewer than
 the device's CUs.  The dQ kernel takes 128-query workgroups of 4 waves, or
 of 8 waves, two per 32 queries splitting every key tile, when its 128-query
-blocks are fewer than the CUs.  Each case asserts both instances first,
+blocks are fewer than twice the CUs.  Each case asserts both instances first,
 then checks sampled (or all) rows and keys of some heads against the
 float64 oracle under the per-element bound of the backward tests.
 """
@@ -32,8 +32,8 @@ def cus():
 
 
 # (B, H, T, d): grids below and above the switches on a 256-CU device
-# (B H = 16, T = 2048: paired dK/dV, unpaired dQ; T = 100: one block, its
-# second 32 rows past the end)
+# (B H = 16, T = 2048: paired dK/dV and dQ; B H = 32: neither; T = 100:
+# one block, its second 32 rows past the end)
 CASES = [(1, 8, 2048, 64), (1, 8, 2048, 128), (2, 3, 700, 128), (1, 1, 5000, 64),
          (1, 32, 2048, 128), (2, 16, 2048, 64), (1, 16, 2048, 64), (1, 2, 100, 128),
          (3, 1, 33, 64)]
@@ -47,7 +47,7 @@ def test_bwd_instances(B, H, T, d, causal):
     small = B * H * ((T + 255) // 256) < cus()
     assert name.endswith("bk128_bq64_w8" if small else "bk256_bq64_w8"), name
     qname = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 2)
-    qsmall = B * H * ((T + 127) // 128) < cus()
+    qsmall = B * H * ((T + 127) // 128) < 2 * cus()
     assert qname.endswith("bq128_bk64_w8" if qsmall else "bq128_bk64_w4"), qname
     say(f"[bwd instance] {name} {qname} B={B} H={H} T={T}")
     scale = 1.0 / math.sqrt(d)
