@@ -2,8 +2,10 @@
 // up to 32 query rows (one MFMA column block) and a range of keys, which its
 // waves (4 or 8) split between them: each wave streams its own 32-key blocks,
 // with no workgroup barrier in the loop -- K straight into registers (the A
-// operand of the score MFMA as loaded), V direct-to-LDS (its transposing
-// read needs LDS), both one block ahead -- and the waves' partial results
+// operand of the score MFMA as loaded) or direct-to-LDS, V direct-to-LDS
+// (its transposing read needs LDS), both one block ahead, and with one wave
+// per SIMD the next block's scores computed during this block's softmax --
+// and the waves' partial results
 // (running max, normalisers, output accumulator) merge in LDS at the end
 // with the rescaling of the online softmax ("Attention Mechanism:
 // Computation & Memory Patterns", section 3: the running max and sum let
