@@ -120,7 +120,7 @@ def cpu_baseline(x, causal: bool, scale: float, heads: int, pass_: str, do_bits=
                                   causal=causal, scale=scale)
         else:
             g = bf16_bits_to_f32(do_bits[b, h]).astype("float64")
-            oracle.attention_head_bwd(x.q64(b, h), x.k64(b, h), x.v64(b, h), g,
+            oracle.attention_head_bwd(x.q64(b, h), x.k64(b, h // G), x.v64(b, h // G), g,
                                       causal=causal, scale=scale)
         done += 1
     dt = time.perf_counter() - t0
@@ -669,9 +669,8 @@ def main() -> int:
     B, H, T, d, dt = w["B"], w["H"], w["T"], w["d"], w["dtype"]
     bwd = args.pass_ == "bwd"
     Hkv = w.get("H_kv", H)
-    if bwd and (dt != "bf16" or Hkv != H):
-        print("bench --pass bwd takes bf16 workloads without grouped key/value heads",
-              file=sys.stderr)
+    if bwd and dt != "bf16":
+        print("bench --pass bwd takes bf16 workloads", file=sys.stderr)
         return 2
     scale = 1.0 / math.sqrt(d)
     dev = torch.device("cuda:0")
@@ -695,12 +694,12 @@ def main() -> int:
     if bwd:
         do_bits = make_dout(B, H, T, d, seed=x.seed + DOUT_SEED_OFFSET)
         dout = up(do_bits)
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(2 * B * H * T, dtype=torch.float32, device=dev)
         ea.forward(q, k, v, causal=causal, scale=scale, out=out, lse=lse)
-        # the instances attn_bwd launches for these sizes on this device
-        kname = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 1)
-        knames = [ea.bwd_kernel_name_for(B, H, H, T, d, causal, i) for i in range(3)]
+        # the instances attn_bwd_gqa launches for these sizes on this device
+        kname = ea.bwd_kernel_name_for(B, H, Hkv, T, d, causal, 1)
+        knames = [ea.bwd_kernel_name_for(B, H, Hkv, T, d, causal, i) for i in range(3)]
         fl = ea.bwd_flops(B, H, T, d, causal)
     else:
         do_bits = None
@@ -742,16 +741,31 @@ def main() -> int:
         else:
             # Relative to the largest reference magnitude of each gradient;
             # the parity tests hold the per-element bound.
+            # (grouped heads: dQ of query head h against its key/value head
+            # h // G; dK, dV of key/value head g sum its G query heads')
             G = [to64(t) for t in (dq, dk, dv)]
+            grp = H // Hkv
             worst = 0.0
+
+            def rel(got, want):
+                return float(np.abs(got - want).max() / np.abs(want).max())
+
             for (b, h) in heads:
                 g = bf16_bits_to_f32(do_bits[b, h]).astype(np.float64)
-                ref = oracle.attention_head_bwd(x.q64(b, h), x.k64(b, h), x.v64(b, h), g,
-                                                causal=causal, scale=scale, rows=rows,
-                                                keys=rows)
-                for got, want in ((G[0][b, h][rows], ref["dQ"]), (G[1][b, h][rows], ref["dK"]),
-                                  (G[2][b, h][rows], ref["dV"])):
-                    worst = max(worst, float(np.abs(got - want).max() / np.abs(want).max()))
+                ref = oracle.attention_head_bwd(x.q64(b, h), x.k64(b, h // grp),
+                                                x.v64(b, h // grp), g, causal=causal,
+                                                scale=scale, rows=rows, keys=rows)
+                worst = max(worst, rel(G[0][b, h][rows], ref["dQ"]))
+            for (b, kh) in ((0, 0), (B - 1, Hkv - 1)):
+                rdk = rdv = 0.0
+                for h in range(kh * grp, (kh + 1) * grp):
+                    g = bf16_bits_to_f32(do_bits[b, h]).astype(np.float64)
+                    ref = oracle.attention_head_bwd(x.q64(b, h), x.k64(b, kh), x.v64(b, kh), g,
+                                                    causal=causal, scale=scale, rows=rows,
+                                                    keys=rows)
+                    rdk = rdk + ref["dK"]
+                    rdv = rdv + ref["dV"]
+                worst = max(worst, rel(G[1][b, kh][rows], rdk), rel(G[2][b, kh][rows], rdv))
             parity = {"rows_checked": int(2 * len(rows)), "keys_checked": int(2 * len(rows)),
                       "max_err_rel_to_max_ref": worst, "pass": bool(worst <= 2e-2)}
         if not parity["pass"]:

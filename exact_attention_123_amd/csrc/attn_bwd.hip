@@ -22,9 +22,10 @@
 //             registers; it walks 64-query tiles of Q and dO (staged in
 //             LDS) and accumulates dV^T += dO^T P and dK^T += Q^T dS in
 //             registers.  When the 256-key blocks of the problem are fewer
-//             than the device's CUs: 128 keys per workgroup, two waves per
-//             32 keys, each taking one half of every query tile, their sums
-//             added at the end.
+//             than the device's CUs (under the causal mask, than twice the
+//             CUs): 128 keys per workgroup, two waves per 32 keys, each
+//             taking one half of every query tile, their sums added at the
+//             end.
 //   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
 //             registers; it walks 64-key tiles of K and V (staged in LDS)
 //             and accumulates dQ^T += K^T dS^T.  When the 128-query blocks
@@ -56,8 +57,7 @@ using attn_internal::device_cus;
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = 4;
 // dkdv: 8 waves per workgroup, 32 keys per wave (256 keys), or two waves
-// per 32 keys (128 keys) when the 256-key blocks would be fewer than the
-// device's CUs
+// per 32 keys (128 keys) for grids of few 256-key blocks (see dkdv_paired)
 constexpr int kDkdvWaves = 8;
 constexpr int kBK = 32 * kDkdvWaves;  // keys per dkdv workgroup (unpaired)
 constexpr int kBQ = 128;       // queries per dq workgroup
@@ -117,9 +117,9 @@ __global__ __launch_bounds__(kThreads) void attn_bwd_prep_kernel(
 // 256 keys are staged in LDS once, each wave holds V of its 32 keys and
 // its dK, dV accumulators in registers, and the staged Q and dO tiles serve
 // all 256 keys.  PAIR (128 keys, two waves per 32 keys) for problems with
-// fewer 256-key blocks than CUs: there the heaviest block's walk over every
-// query tile sets the time; a 128-key block halves the walk and the pair's
-// split of every tile halves each wave's share again.  Measured on MI355X
+// few 256-key blocks (see dkdv_paired): there the heaviest block's walk over
+// every query tile sets the time; a 128-key block halves the walk and the
+// pair's split of every tile halves each wave's share again.  Measured on MI355X
 // (us per call of the whole backward, paired / 4 waves of 32 keys per
 // 128-key block, dQ likewise paired / not): B H = 8, T = 2048, causal,
 // d = 64 65.0 / 83.0, d = 128 99.9 / 119.9; no mask, d = 64 64.2 / 82.7;
@@ -630,12 +630,21 @@ const void* dkdv_kernel(int causal, bool fold, bool pair) {
 }
 
 // Paired waves (128 keys per workgroup, two waves per 32 keys) when the
-// 256-key blocks of all key/value heads are fewer than the CUs: there the
-// heaviest block's walk over every query tile sets the time, and a
-// 128-key block with the tiles' halves split between two waves shortens
-// each wave's walk to a quarter.
-bool dkdv_paired(int64_t BHkv, int64_t T) {
-  return BHkv * ((T + kBK - 1) / kBK) < device_cus();
+// 256-key blocks of all key/value heads are fewer than the CUs, or, under
+// the causal mask, fewer than twice the CUs: there the heaviest block's
+// walk over every query tile sets the time (under the mask the first block
+// of a head walks every tile, the last one a few, and one or two rounds of
+// blocks cannot even that out), and a 128-key block with the tiles' halves
+// split between two waves shortens each wave's walk to a quarter.
+// Measured on MI355X (us per call of the backward, causal, d = 128; paired
+// below 2 / below 1 CU count): 32 query over 8 key/value heads, T = 8192
+// (256 blocks, each walking 4 query heads) 1655.8 / 2109.3; B H = 8,
+// T = 8192 492.5 / 595.1; B H = 48, T = 2048 (384 blocks) 231.1 / 245.8;
+// B H = 12, T = 8192 678.6 / 686.3; 512 blocks (B H = 16, T = 8192) the
+// same; unmasked, 256 blocks (32 over 8 heads, T = 8192) 3329 against 3235
+// paired, so without the mask only grids below the CU count pair.
+bool dkdv_paired(int64_t BHkv, int64_t T, int causal) {
+  return BHkv * ((T + kBK - 1) / kBK) < (causal ? 2 : 1) * device_cus();
 }
 template <int D, bool PAIR>
 const void* dq_kernel(int causal) {
@@ -721,7 +730,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
                *gb = (const __bf16*)dout;
   const float* wsc = ws;
   {
-    const bool pair = dkdv_paired(BHkv, T);
+    const bool pair = dkdv_paired(BHkv, T, causal);
     const int bk = pair ? kBK / 2 : kBK;
     int nkb = (int)((T + bk - 1) / bk);
     __bf16 *dkb = (__bf16*)dk, *dvb = (__bf16*)dv;
@@ -778,7 +787,7 @@ const char* attn_bwd_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t
   if (B <= 0 || H <= 0 || H_kv <= 0 || T <= 0 || H % H_kv != 0) return nullptr;
   const char* name = attn_bwd_kernel_name(d, causal, which);
   if (name == nullptr || check_device() != ATTN_OK) return nullptr;
-  if (which == 1 && dkdv_paired(B * H_kv, T)) {
+  if (which == 1 && dkdv_paired(B * H_kv, T, causal)) {
     static const char* small[2][2] = {
         {"attn_bwd_dkdv_bf16_d64_full_bk128_bq64_w8",
          "attn_bwd_dkdv_bf16_d64_causal_bk128_bq64_w8"},
