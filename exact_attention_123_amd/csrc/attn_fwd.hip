@@ -1031,10 +1031,20 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
 // already fills the CUs twice in d = 64 units.
 enum class FwdPlan { kWaves8, kWaves4, kRows };
 
-FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d) {
+// The 4-wave instance also takes one full round of 256-row blocks under the
+// causal mask from T = 4096 on: there a head's last block walks every key
+// tile and its first a few, the heaviest sets the time, and the 128-row
+// blocks halve it.  Measured on MI355X (us per launch, 4-wave / 8-wave, B H
+// ceil(T / 256) = 256, causal): d = 128, T = 4096 91.4 / 105.9, T = 8192
+// 167.7 / 199.5, T = 32768 625.7 / 760.4; d = 64, T = 4096 63.2 / 74.0; but
+// T = 2048 55.6 / 58.4 at d = 128 and 44.5 / 41.2 at d = 64, T = 1024
+// 46.3 / 36.7; and at 384 blocks (one and a half rounds) 267.5 / 222.9.
+FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d, int causal) {
   const int64_t cus = device_cus();
   if (B * H * ((T + 127) / 128) * (d / 64) <= cus) return FwdPlan::kRows;
-  return B * H * ((T + 255) / 256) < cus ? FwdPlan::kWaves4 : FwdPlan::kWaves8;
+  const int64_t blocks = B * H * ((T + 255) / 256);
+  return blocks < cus || (causal && blocks == cus && T >= 4096) ? FwdPlan::kWaves4
+                                                                : FwdPlan::kWaves8;
 }
 
 // The fp32 forward takes the row-chunk kernel (32 rows per workgroup, keys
@@ -1185,14 +1195,14 @@ attn_status fwd_over_cache(const void* q, const void* k, const void* v, void* o,
                            int64_t Tk_cap, int64_t d, int causal, float scale,
                            hipStream_t stream) {
   if (check_device() != ATTN_OK) return ATTN_ERR_DEVICE;
-  const int nw = pick_plan(B, H, Tq, d) == FwdPlan::kWaves8 ? 8 : 4;
+  const int nw = pick_plan(B, H, Tq, d, 0) == FwdPlan::kWaves8 ? 8 : 4;
   return launch_bf16(nw, d, causal, scale, q, k, v, o, lse, B, H, H_kv, Tq, Tk, Tk_cap,
                      causal ? Tk - Tq : 0, stream);
 }
 
 const char* fwd_over_cache_kernel_name(int64_t B, int64_t H, int64_t Tq, int64_t d, int causal) {
   if (check_device() != ATTN_OK) return nullptr;
-  if (pick_plan(B, H, Tq, d) == FwdPlan::kWaves8) return attn_kernel_name(0, d, causal);
+  if (pick_plan(B, H, Tq, d, 0) == FwdPlan::kWaves8) return attn_kernel_name(0, d, causal);
   return w4_kernel_name(d, causal);
 }
 
@@ -1207,7 +1217,7 @@ attn_status attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, f
   attn_status st = validate(q, k, v, o, lse, B, H, H_kv, T, d, causal, scale, 2, empty);
   if (st != ATTN_OK || empty) return st;
   if ((st = check_device()) != ATTN_OK) return st;
-  const FwdPlan plan = pick_plan(B, H, T, d);
+  const FwdPlan plan = pick_plan(B, H, T, d, causal);
   if (plan == FwdPlan::kRows)
     return launch_rows(d, causal, q, k, v, o, lse, B, H, H_kv, T, scale, stream);
   const int nw = plan == FwdPlan::kWaves4 ? 4 : 8;
@@ -1256,7 +1266,7 @@ const char* attn_fwd_kernel_name_for(int64_t B, int64_t H, int64_t T, int64_t d,
     return nullptr;
   if (B > (int64_t(1) << 31) / H || T > (int64_t(1) << 31)) return nullptr;
   if (check_device() != ATTN_OK) return nullptr;
-  const FwdPlan plan = pick_plan(B, H, T, d);
+  const FwdPlan plan = pick_plan(B, H, T, d, causal);
   if (plan == FwdPlan::kWaves8) return attn_kernel_name(0, d, causal);
   static const char* rows[2][2][2] = {
       {{"attn_fwd_rows_bf16_d64_full_br32_bc32_w4", "attn_fwd_rows_bf16_d64_causal_br32_bc32_w4"},

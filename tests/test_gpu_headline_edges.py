@@ -191,3 +191,39 @@ def test_decode_forward_route_running_max(name):
         el = max(el, float(np.abs(L[0, h] - ref["LSE"]).max()))
     say(f"    max|O err|={eo:.3e} max|LSE err|={el:.3e}")
     assert eo <= TOL_O and el <= TOL_LSE
+
+
+@pytest.mark.parametrize("B,H,T,d,causal,inst", [(1, 8, 8192, 128, True, "w4"),
+                                                (1, 16, 4096, 64, True, "w4"),
+                                                (1, 8, 8192, 128, False, "w8"),
+                                                (1, 32, 2048, 128, True, "w8")])
+def test_one_round_causal_grid(B, H, T, d, causal, inst):
+    """One round of 256-row blocks (B H ceil(T / 256) equal to the CU
+    count): under the causal mask from T = 4096 on the 4-wave instance runs
+    it (the heaviest 256-row block would set the time), otherwise the
+    8-wave one; sampled rows of every head against the oracle."""
+    import torch
+
+    import exact_attention_123_amd as ea
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if B * H * ((T + 255) // 256) != cus:
+        pytest.skip(f"a one-round grid needs {cus} blocks on this device")
+    name = ea.fwd_kernel_name_for(B, H, T, d, causal)
+    assert name.endswith(SUFFIX[inst]), name
+    say(f"[one-round grid] {name} B={B} H={H} T={T}")
+    x = make_qkv(B, H, T, d, dtype="bf16", seed=9700 + T + d, qk_mult=4.0)
+    qd, kd, vd = (to_device(a, "bf16") for a in (x.q, x.k, x.v))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = ea.forward(qd, kd, vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    O = o.float().cpu().numpy().astype(np.float64)
+    L = lse.cpu().numpy().astype(np.float64)
+    rng = np.random.Generator(np.random.PCG64(9701))
+    rows = np.unique(np.r_[0, 127, 128, 255, 256, T - 129, T - 128, T - 1,
+                           rng.choice(T, 40, replace=False)])
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.attention_head(x.q64(b, h), x.k64(b, h), x.v64(b, h), causal=causal,
+                                        scale=scale, rows=rows)
+            assert np.abs(O[b, h, rows] - ref["O"]).max() <= TOL_O, (b, h)
+            assert np.abs(L[b, h, rows] - ref["LSE"]).max() <= TOL_LSE, (b, h)
