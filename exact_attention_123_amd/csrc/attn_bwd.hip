@@ -29,8 +29,9 @@
 //   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
 //             registers; it walks 64-key tiles of K and V (staged in LDS)
 //             and accumulates dQ^T += K^T dS^T.  When the 128-query blocks
-//             are fewer than twice the CUs: two waves per 32 queries, each
-//             taking one half of every key tile.
+//             are fewer than twice the CUs (under the causal mask, at most
+//             twice): two waves per 32 queries, each taking one half of
+//             every key tile.
 // dkdv and dq each recompute S and dP for their tiles; neither needs
 // atomics or a second pass, and every output element is written by exactly
 // one lane (the result does not depend on scheduling).
@@ -658,13 +659,15 @@ const void* dq_kernel(int causal, bool pair) {
 
 // Paired waves in the dQ kernel (8 per 128 queries) when its 128-query
 // blocks are fewer than twice the CUs (the unpaired kernel's two
-// workgroups per CU).  Measured on MI355X (us per call of the backward,
-// paired below 2 / 1 CU count): B H = 16, T = 2048, causal, d = 64
-// 65.9 / 70.8, d = 128 103.5 / 111.7; B H = 8, T = 4096, d = 128
-// 183.7 / 201.4; B H = 24, T = 2048, d = 128 131.7 / 140.2; the same at
-// 512 blocks and more, where neither pairs.
-bool dq_paired(int64_t BH, int64_t T) {
-  return BH * ((T + kBQ - 1) / kBQ) < 2 * device_cus();
+// workgroups per CU), or, under the causal mask, exactly twice as many (one
+// round whose blocks the mask makes unequal).  Measured on MI355X (us per
+// call of the backward, paired below 2 / 1 CU count): B H = 16, T = 2048,
+// causal, d = 64 65.9 / 70.8, d = 128 103.5 / 111.7; B H = 8, T = 4096,
+// d = 128 183.7 / 201.4; B H = 24, T = 2048, d = 128 131.7 / 140.2; at 512
+// blocks, causal (paired / not): B H = 32, T = 2048, d = 128 163.0 / 177.5,
+// d = 64 98.8 / 109.0; B H = 8, T = 8192 444.5 / 480.4; at 768 the same.
+bool dq_paired(int64_t BH, int64_t T, int causal) {
+  return BH * ((T + kBQ - 1) / kBQ) < 2 * device_cus() + (causal ? 1 : 0);
 }
 
 }  // namespace
@@ -750,7 +753,7 @@ attn_status attn_bwd_gqa(const void* q, const void* k, const void* v, const void
     void* args[] = {(void*)&qb, (void*)&kb_, (void*)&vb,  (void*)&gb, (void*)&wsc,
                     (void*)&dqb, (void*)&t,  (void*)&bh,  (void*)&nqb, (void*)&g,
                     (void*)&c,  (void*)&cw, (void*)&scale};
-    const bool pair = dq_paired(BH, T);
+    const bool pair = dq_paired(BH, T, causal);
     const void* kern = d == 64 ? dq_kernel<64>(causal, pair) : dq_kernel<128>(causal, pair);
     if (hipLaunchKernel(kern, dim3((unsigned)(bh * nqb)), dim3(pair ? 2 * kThreads : kThreads),
                         args, 0, stream) != hipSuccess)
@@ -795,7 +798,7 @@ const char* attn_bwd_kernel_name_for(int64_t B, int64_t H, int64_t H_kv, int64_t
          "attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w8"}};
     return small[d == 128 ? 1 : 0][causal];
   }
-  if (which == 2 && dq_paired(B * H, T)) {
+  if (which == 2 && dq_paired(B * H, T, causal)) {
     static const char* small[2][2] = {
         {"attn_bwd_dq_bf16_d64_full_bq128_bk64_w8", "attn_bwd_dq_bf16_d64_causal_bq128_bk64_w8"},
         {"attn_bwd_dq_bf16_d128_full_bq128_bk64_w8",

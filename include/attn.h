@@ -181,7 +181,8 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
  * workgroups of 8 waves, two per 32 keys
  * ("attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w8"); the dQ kernel takes
  * 128-query workgroups of 4 waves, or, when B * H * ceil(T / 128) is below
- * twice the CU count, of 8 waves, two per 32 queries
+ * twice the CU count (with causal = 1, at most twice), of 8 waves, two per
+ * 32 queries
  * ("attn_bwd_dq_bf16_d128_causal_bq128_bk64_w8").  NULL for unsupported or
  * non-positive sizes, or when the current device is not a gfx950.
  */

@@ -5,7 +5,7 @@ each), or 128-key workgroups of 8 waves, two per 32 keys splitting every
 query tile, when the 256-key blocks of all key/value heads are fewer than
 the device's CUs (under the causal mask, than twice the CUs).  The dQ kernel takes 128-query workgroups of 4 waves, or
 of 8 waves, two per 32 queries splitting every key tile, when its 128-query
-blocks are fewer than twice the CUs.  Each case asserts both instances first,
+blocks are fewer than twice the CUs (under the causal mask, at most twice).  Each case asserts both instances first,
 then checks sampled (or all) rows and keys of some heads against the
 float64 oracle under the per-element bound of the backward tests.
 """
@@ -48,7 +48,7 @@ def test_bwd_instances(B, H, T, d, causal):
     small = B * H * ((T + 255) // 256) < (2 if causal else 1) * cus()
     assert name.endswith("bk128_bq64_w8" if small else "bk256_bq64_w8"), name
     qname = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 2)
-    qsmall = B * H * ((T + 127) // 128) < 2 * cus()
+    qsmall = B * H * ((T + 127) // 128) < 2 * cus() + (1 if causal else 0)
     assert qname.endswith("bq128_bk64_w8" if qsmall else "bq128_bk64_w4"), qname
     say(f"[bwd instance] {name} {qname} B={B} H={H} T={T}")
     scale = 1.0 / math.sqrt(d)
