@@ -23,9 +23,9 @@
 //             LDS) and accumulates dV^T += dO^T P and dK^T += Q^T dS in
 //             registers.  When the 256-key blocks of the problem are fewer
 //             than the device's CUs (under the causal mask, than twice the
-//             CUs): 128 keys per workgroup, two waves per 32 keys, each
-//             taking one half of every query tile, their sums added at the
-//             end.
+//             CUs, or at most four times with T <= 4096): 128 keys per
+//             workgroup, two waves per 32 keys, each taking one half of
+//             every query tile, their sums added at the end.
 //   3. dq   : one workgroup per 128 queries (32 per wave), Q and dO in
 //             registers; it walks 64-key tiles of K and V (staged in LDS)
 //             and accumulates dQ^T += K^T dS^T.  When the 128-query blocks
@@ -643,9 +643,20 @@ const void* dkdv_kernel(int causal, bool fold, bool pair) {
 // T = 8192 492.5 / 595.1; B H = 48, T = 2048 (384 blocks) 231.1 / 245.8;
 // B H = 12, T = 8192 678.6 / 686.3; 512 blocks (B H = 16, T = 8192) the
 // same; unmasked, 256 blocks (32 over 8 heads, T = 8192) 3329 against 3235
-// paired, so without the mask only grids below the CU count pair.
+// paired, so without the mask only grids below the CU count pair.  Under
+// the mask short sequences (T <= 4096: a 256-key block walks at most 64
+// query tiles, so its fixed costs weigh more) pair up to four times the CU
+// count: B H = 32, T = 4096 459.4 / 513.2 (d = 128), 276.3 / 321.0
+// (d = 64); B H = 64, T = 2048 286.0 / 303.8 and 178.2 / 190.8; B H = 48,
+// T = 4096 696.0 / 719.9 and 395.6 / 424.4; B H = 64, T = 4096 (1024
+// blocks) 920.7 / 935.1 and 518.7 / 551.0; B H = 128, T = 2048 570.5 /
+// 559.7 and 320.2 / 332.4.  Longer sequences keep the larger blocks: the
+// T = 8192 workload (1024 blocks) 1740.7 paired / 1666.1, B H = 8,
+// T = 65536 25103 / 24216, B H = 16, T = 8192 (512 blocks) 847.3 / 823.4.
 bool dkdv_paired(int64_t BHkv, int64_t T, int causal) {
-  return BHkv * ((T + kBK - 1) / kBK) < (causal ? 2 : 1) * device_cus();
+  const int64_t blocks = BHkv * ((T + kBK - 1) / kBK), cus = device_cus();
+  if (!causal) return blocks < cus;
+  return blocks < 2 * cus || (T <= 4096 && blocks <= 4 * cus);
 }
 template <int D, bool PAIR>
 const void* dq_kernel(int causal) {

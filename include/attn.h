@@ -177,8 +177,9 @@ const char* attn_bwd_kernel_name(int64_t d, int causal, int which);
  * actually selected ("FlashAttention -- avoid writing the giant
  * intermediate", "Apply it at the right layer").  The dK/dV kernel takes
  * 256-key workgroups of 8 waves, or, when B * H_kv * ceil(T / 256) is below
- * the device's CU count (with causal = 1, below twice the CU count), 128-key
- * workgroups of 8 waves, two per 32 keys
+ * the device's CU count (with causal = 1, below twice the CU count, or at
+ * most four times it with T <= 4096), 128-key workgroups of 8 waves, two per
+ * 32 keys
  * ("attn_bwd_dkdv_bf16_d128_causal_bk128_bq64_w8"); the dQ kernel takes
  * 128-query workgroups of 4 waves, or, when B * H * ceil(T / 128) is below
  * twice the CU count (with causal = 1, at most twice), of 8 waves, two per

@@ -6,7 +6,7 @@ each first asserting by name which instance its sizes select:
 
   - the 8-wave dK/dV kernel with the unfolded exponent: |scale| < 2^-32
     (zero, 1e-12) on grids with at least as many 256-key blocks as CUs
-    (twice as many under the causal mask),
+    (twice as many, and T > 4096, under the causal mask),
     both masks, d in {64, 128}; gradients against the float64 backward
     oracle under the per-element bound of the backward tests;
   - the row-chunk forward with 8 waves at d = 128 without a mask (grids
@@ -53,9 +53,10 @@ def cus():
 @pytest.mark.parametrize("d", [64, 128])
 def test_dkdv_w8_unfolded(d, causal, scale):
     import exact_attention_123_amd as ea
-    # 256 key blocks of 256 (ragged end); under the causal mask 512, since
-    # causal grids below twice the CU count take the paired instance
-    B, H, T = 1, 64 if causal else 32, 2000
+    # 256 key blocks of 256 (ragged end); under the causal mask 576 of a
+    # sequence longer than 4096, since shorter or smaller causal grids take
+    # the paired instance
+    B, H, T = (1, 32, 4500) if causal else (1, 32, 2000)
     assert B * H * ((T + 255) // 256) >= (2 if causal else 1) * cus()
     name = ea.bwd_kernel_name_for(B, H, H, T, d, causal, 1)
     assert name.endswith("_bk256_bq64_w8"), name
