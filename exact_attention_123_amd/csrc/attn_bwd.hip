@@ -643,10 +643,12 @@ const void* dkdv_kernel(int causal, bool fold, bool pair) {
 // T = 8192 492.5 / 595.1; B H = 48, T = 2048 (384 blocks) 231.1 / 245.8;
 // B H = 12, T = 8192 678.6 / 686.3; 512 blocks (B H = 16, T = 8192) the
 // same; unmasked, 256 blocks (32 over 8 heads, T = 8192) 3329 against 3235
-// paired, so without the mask only grids below the CU count pair.  Under
-// the mask short sequences (T <= 4096: a 256-key block walks at most 64
-// query tiles, so its fixed costs weigh more) pair up to four times the CU
-// count: B H = 32, T = 4096 459.4 / 513.2 (d = 128), 276.3 / 321.0
+// paired, so without the mask only grids below the CU count pair (pairing
+// costs 4-7% where the blocks are equal: more Q/dO staging per FLOP; B H =
+// 64, T = 4096 1734.6 / 1616.0, B H = 32, T = 4096, d = 64 483.1 / 462.3).
+// Under the mask short sequences (T <= 4096, walks of at most 64 query
+// tiles, where the finer blocks even out the unequal causal work by more
+// than the pairing costs) pair up to four times the CU count: B H = 32, T = 4096 459.4 / 513.2 (d = 128), 276.3 / 321.0
 // (d = 64); B H = 64, T = 2048 286.0 / 303.8 and 178.2 / 190.8; B H = 48,
 // T = 4096 696.0 / 719.9 and 395.6 / 424.4; B H = 64, T = 4096 (1024
 // blocks) 920.7 / 935.1 and 518.7 / 551.0; B H = 128, T = 2048 570.5 /
