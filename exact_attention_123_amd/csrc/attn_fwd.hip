@@ -1019,10 +1019,12 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
 // one wave walks key tile after key tile:
 //  - the row-chunk kernel (32 query rows per workgroup, their keys split
 //    over its 4 waves: a quarter of that chain, 8x the workgroups of the
-//    8-wave kernel, but no software pipeline between the two contractions)
-//    when the 4-wave grid, counted in d = 64 units, fits the CUs once;
+//    8-wave kernel, with a software pipeline between the two contractions
+//    only at d = 128) when the 4-wave grid, counted in d = 64 units, fits
+//    the CUs once;
 //  - else the 4-wave kernel (128 rows, one wave per SIMD) when the 8-wave
-//    grid has fewer workgroups than the device has CUs;
+//    grid has fewer workgroups than the device has CUs (or, causal with
+//    T >= 4096, as many);
 //  - else the 8-wave kernel.
 // Measured on MI355X (average launch, bf16): the row-chunk kernel takes
 // 16 us against 37 us (4-wave) at B H = 8, T = 2048, d = 64, causal, 167
