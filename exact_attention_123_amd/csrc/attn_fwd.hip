@@ -1024,7 +1024,7 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
 //    the CUs once;
 //  - else the 4-wave kernel (128 rows, one wave per SIMD) when the 8-wave
 //    grid has fewer workgroups than the device has CUs (or, causal with
-//    T >= 4096, as many);
+//    T >= 2048 at d = 128, T >= 4096 at d = 64, as many);
 //  - else the 8-wave kernel.
 // Measured on MI355X (average launch, bf16): the row-chunk kernel takes
 // 16 us against 37 us (4-wave) at B H = 8, T = 2048, d = 64, causal, 167
@@ -1034,19 +1034,20 @@ attn_status validate(const void* q, const void* k, const void* v, const void* o,
 enum class FwdPlan { kWaves8, kWaves4, kRows };
 
 // The 4-wave instance also takes one full round of 256-row blocks under the
-// causal mask from T = 4096 on: there a head's last block walks every key
-// tile and its first a few, the heaviest sets the time, and the 128-row
-// blocks halve it.  Measured on MI355X (us per launch, 4-wave / 8-wave, B H
-// ceil(T / 256) = 256, causal): d = 128, T = 4096 91.4 / 105.9, T = 8192
-// 167.7 / 199.5, T = 32768 625.7 / 760.4; d = 64, T = 4096 63.2 / 74.0; but
-// T = 2048 55.6 / 58.4 at d = 128 and 44.5 / 41.2 at d = 64, T = 1024
-// 46.3 / 36.7; and at 384 blocks (one and a half rounds) 267.5 / 222.9.
+// causal mask from T = 2048 on at d = 128 and T = 4096 at d = 64: there a
+// head's last block walks every key tile and its first a few, the heaviest
+// sets the time, and the 128-row blocks halve it.  Measured on MI355X (us
+// per launch, 4-wave / 8-wave, B H ceil(T / 256) = 256, causal): d = 128,
+// T = 2048 55.4-55.6 / 58.0-58.8, T = 4096 91.4 / 105.9, T = 8192
+// 167.7 / 199.5, T = 32768 625.7 / 760.4; d = 64, T = 4096 63.2 / 74.0;
+// but d = 64, T = 2048 44.5 / 41.2, d = 128, T = 1024 46.3 / 36.7; and at
+// 384 blocks (one and a half rounds) 267.5 / 222.9.
 FwdPlan pick_plan(int64_t B, int64_t H, int64_t T, int64_t d, int causal) {
   const int64_t cus = device_cus();
   if (B * H * ((T + 127) / 128) * (d / 64) <= cus) return FwdPlan::kRows;
   const int64_t blocks = B * H * ((T + 255) / 256);
-  return blocks < cus || (causal && blocks == cus && T >= 4096) ? FwdPlan::kWaves4
-                                                                : FwdPlan::kWaves8;
+  const bool one_round = causal && blocks == cus && T >= (d == 128 ? 2048 : 4096);
+  return blocks < cus || one_round ? FwdPlan::kWaves4 : FwdPlan::kWaves8;
 }
 
 // The fp32 forward takes the row-chunk kernel (32 rows per workgroup, keys

@@ -334,8 +334,9 @@ const char* attn_kernel_name(int is_f32, int64_t d, int causal);
  *     B * H * ceil(T / 128) * (d / 64) is at most the device's CU count;
  *   - else the 4-wave instance (128 rows, e.g.
  *     "attn_fwd_bf16_d128_causal_br128_bc64_w4") when B * H * ceil(T / 256)
- *     is below the CU count, or equal to it with causal = 1 and T >= 4096
- *     (one round of blocks whose work the mask makes unequal);
+ *     is below the CU count, or equal to it with causal = 1 and T >= 2048
+ *     (d = 128) or T >= 4096 (d = 64): one round of blocks whose work the
+ *     mask makes unequal;
  *   - else the 8-wave instance (256 query rows per workgroup).
  * NULL if the sizes are unsupported or the current device is not a gfx950.
  */

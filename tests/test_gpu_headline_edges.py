@@ -195,13 +195,15 @@ def test_decode_forward_route_running_max(name):
 
 @pytest.mark.parametrize("B,H,T,d,causal,inst", [(1, 8, 8192, 128, True, "w4"),
                                                 (1, 16, 4096, 64, True, "w4"),
+                                                (1, 32, 2048, 128, True, "w4"),
                                                 (1, 8, 8192, 128, False, "w8"),
-                                                (1, 32, 2048, 128, True, "w8")])
+                                                (1, 32, 2048, 64, True, "w8")])
 def test_one_round_causal_grid(B, H, T, d, causal, inst):
     """One round of 256-row blocks (B H ceil(T / 256) equal to the CU
-    count): under the causal mask from T = 4096 on the 4-wave instance runs
-    it (the heaviest 256-row block would set the time), otherwise the
-    8-wave one; sampled rows of every head against the oracle."""
+    count): under the causal mask from T = 2048 on at d = 128 (T = 4096 at
+    d = 64) the 4-wave instance runs it (the heaviest 256-row block would
+    set the time), otherwise the 8-wave one; sampled rows of every head
+    against the oracle."""
     import torch
 
     import exact_attention_123_amd as ea
